@@ -1,0 +1,375 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 data path on one MI355X.
+
+Default workload (one "step"): one KV-cache chunk of 8 latent frames x 880
+tokens = 7040 tokens, 24 heads x 128, K and V in bf16 -- K-smoothing
+statistics, NVFP4 4/6 quantization of K_s and V into a ring slot
+(kv_store_chunk), then dequantization of the chunk back to bf16
+(gather_window of the next step, window of one chunk, no sinks).  Inputs are
+resident in HBM before the timed region; four buffer sets are rotated so
+consecutive steps do not hit the 256 MB last-level cache with the previous
+step's data.
+
+Prints one JSON line.  `value` is algorithmic GB/s of the whole step (one read
+of every input, one write of every output).  `roofline` is the dominant
+kernel: algorithmic bytes per launch / its mean launch time from HIP events
+recorded around each launch on the launch's own stream, against 8 TB/s.
+`cpu_baseline` times the CPU oracle (test infrastructure, single thread) on a
+bounded sample.  `secondary` carries the W4A4 GEMM (7040x3072x3072, TFLOP/s
+vs the 2.5 PFLOP/s dense fp16/bf16 MFMA peak) and activation quantize lines.
+
+Other workloads (--workload): gemm_attn, ffn, ring64s, quant_act.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+METRIC = "NVFP4 quant/dequant GB/s (% HBM peak); W4A4 GEMM TFLOP/s (% bf16 MFMA peak)"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="kv_chunk",
+                    choices=["kv_chunk", "gemm_attn", "ffn", "ring64s", "quant_act"])
+    ap.add_argument("--sets", type=int, default=4, help="rotated input/output buffer sets")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------------------
+# helpers
+# --------------------------------------------------------------------------
+
+def bf16_from_bits(bits, device):
+    import numpy as np
+    import torch
+
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def time_steps(step_fn, steps, warmup):
+    """Mean ms per step over `steps` steps bracketed by synchronisations."""
+    import torch
+
+    for i in range(warmup):
+        step_fn(i)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record(s)
+    for i in range(steps):
+        step_fn(warmup + i)
+    e1.record(s)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - w0) * 1e3
+    return e0.elapsed_time(e1) / steps, wall / steps
+
+
+def kernel_times(nv, step_fn, steps, base):
+    """Per-kernel mean launch time (ms) from the library's event timing."""
+    import torch
+
+    torch.cuda.synchronize()
+    nv.profile_collect()
+    nv.profile_enable(True)
+    for i in range(steps):
+        step_fn(base + i)
+    torch.cuda.synchronize()
+    nv.profile_enable(False)
+    rec = nv.profile_collect()
+    return {k: (n, ms / n) for k, (n, ms) in rec.items() if n}
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, alg_bytes):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get("kernels", {}).get(kernel)
+    if not ent or ent.get("source_hash") != source_hash(data.get("sources", [])):
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+# --------------------------------------------------------------------------
+# workloads
+# --------------------------------------------------------------------------
+
+KV_T, KV_H, KV_D = 7040, 24, 128
+
+
+def kv_bytes_per_chunk(T=KV_T, H=KV_H, D=KV_D):
+    """Algorithmic bytes of storing (or dequantizing) one chunk: bf16 K and V
+    (2 B/element) on one side, packed NVFP4 ((9/8) B per K+V element pair,
+    i.e. 0.5625 B/element) plus the key mean (fp32 [H*D]) and two fp32 tensor
+    scales on the other."""
+    elems = 2 * T * H * D
+    return elems * 2 + elems * 9 // 16 + H * D * 4 + 8
+
+
+def setup_kv_chunk(nv, args, dev):
+    import numpy as np
+    import torch
+
+    import synth
+
+    kb, vb = synth.kv_chunk(1002, 0, KV_T, KV_H, KV_D)
+    K0, V0 = bf16_from_bits(kb, dev), bf16_from_bits(vb, dev)
+    Ks = [K0.clone() for _ in range(args.sets)]
+    Vs = [V0.clone() for _ in range(args.sets)]
+    Ko = [torch.empty_like(K0) for _ in range(args.sets)]
+    Vo = [torch.empty_like(V0) for _ in range(args.sets)]
+    cfg = nv.KVConfig(sink_frames_global=0, sink_frames_shot=0, window_chunks=1)
+    ring = nv.KVRing(cfg)
+    state = {"t": 0}
+
+    def step(i):
+        j = i % args.sets
+        t = state["t"]
+        ring.store_chunk(t, Ks[j], Vs[j])
+        ring.gather_window(t + 1, Ko[j], Vo[j])
+        state["t"] = t + 1
+
+    return step, {"K": kb, "V": vb}
+
+
+def cpu_baseline_kv(sample_tokens=880):
+    """The oracle (single-threaded C) on one frame's worth of tokens of the
+    chunk: K-smoothing + 4/6 quantization of K and V, then dequantization of
+    both back to bf16.  Returned in GB/s of the same algorithmic bytes."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    kb, vb = synth.kv_chunk(1002, 0, sample_tokens, KV_H, KV_D)
+    K = synth.bf16_bits_to_f32(kb).reshape(sample_tokens, -1)
+    V = synth.bf16_bits_to_f32(vb).reshape(sample_tokens, -1)
+    oracle.lib()
+    t0 = time.perf_counter()
+    ch = oracle.kv_encode_chunk(K, V)
+    oracle.kv_dequant_tokens(ch, 0, sample_tokens, key=True)
+    oracle.kv_dequant_tokens(ch, 0, sample_tokens, key=False)
+    dt = time.perf_counter() - t0
+    alg = 2 * kv_bytes_per_chunk(T=sample_tokens)
+    return {"value": alg / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"one 880-token frame of the chunk ({sample_tokens}x{KV_H}x{KV_D} K and V, "
+                      f"store + dequantize), {dt:.1f} s single-threaded"}
+
+
+def setup_gemm(nv, dev, M=7040, N=3072, K=3072, seed=1003):
+    import torch
+
+    import synth
+
+    X = torch.from_numpy(synth.activations(seed, 0, M, K, 0.005, 30.0)).to(dev).to(torch.bfloat16)
+    W = torch.from_numpy(synth.weights(seed, 1, N, K)).to(dev).to(torch.bfloat16)
+    qa = nv.quantize(X)
+    qw = nv.quantize(W, layout=nv.LAYOUT_2D)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    return X, qa, qw, Y
+
+
+def run_gemm_attn(nv, args, dev):
+    M, N, K = 7040, 3072, 3072
+    X, qa, qw, Y = setup_gemm(nv, dev, M, N, K)
+
+    def step(i):
+        nv.gemm_w4a4(qa, qw, out=Y)
+
+    ms, wall = time_steps(step, args.steps, args.warmup)
+    kt = kernel_times(nv, step, max(5, args.steps // 5), 0)
+    flops = 2.0 * M * N * K
+    kms = kt["gemm_w4a4"][1]
+    return {"ms": ms, "wall_ms": wall, "tflops": flops / ms / 1e9, "kernel_ms": kms,
+            "kernel_tflops": flops / kms / 1e9, "flops": flops, "kernels": kt}
+
+
+def run_quant_act(nv, args, dev, M=7040, K=3072):
+    import torch
+
+    import synth
+
+    X = torch.from_numpy(synth.activations(1003, 0, M, K, 0.005, 30.0)).to(dev).to(torch.bfloat16)
+    Xs = [X.clone() for _ in range(args.sets)]
+    outs = [nv.NVFP4Tensor.empty(M, K) for _ in range(args.sets)]
+    ws = torch.empty(nv.quantize_workspace_bytes(M, K), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        j = i % args.sets
+        nv.quantize(Xs[j], out=outs[j], workspace=ws)
+
+    ms, wall = time_steps(step, args.steps, args.warmup)
+    kt = kernel_times(nv, step, max(5, args.steps // 5), 0)
+    alg = M * K * 2 + M * K // 2 + M * K // 16 + 4
+    return {"ms": ms, "wall_ms": wall, "gbs": alg / ms / 1e6, "alg_bytes": alg, "kernels": kt}
+
+
+def run_ffn(nv, args, dev):
+    import torch
+
+    import synth
+
+    M, K, F = 7040, 3072, 14336
+    X = torch.from_numpy(synth.activations(1004, 0, M, K, 0.005, 30.0)).to(dev).to(torch.bfloat16)
+    Wu = torch.from_numpy(synth.weights(1004, 1, F, K)).to(dev).to(torch.bfloat16)
+    Wd = torch.from_numpy(synth.weights(1004, 2, K, F)).to(dev).to(torch.bfloat16)
+    qx = nv.quantize(X)
+    qu = nv.quantize(Wu, layout=nv.LAYOUT_2D)
+    qd = nv.quantize(Wd, layout=nv.LAYOUT_2D)
+    H = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
+    qh = nv.NVFP4Tensor.empty(M, F)
+    ws = torch.empty(nv.quantize_workspace_bytes(M, F), dtype=torch.uint8, device=dev)
+    Y = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        nv.gemm_w4a4(qx, qu, out=H)
+        nv.quantize(H, out=qh, workspace=ws)
+        nv.gemm_w4a4(qh, qd, out=Y)
+
+    ms, wall = time_steps(step, args.steps, args.warmup)
+    kt = kernel_times(nv, step, max(3, args.steps // 5), 0)
+    flops = 2.0 * 2 * M * K * F
+    return {"ms": ms, "wall_ms": wall, "tflops": flops / ms / 1e9, "flops": flops, "kernels": kt}
+
+
+def run_ring64s(nv, args, dev):
+    """40 chunks; cuts every 10 chunks; per step: gather K_eff(t), store chunk t."""
+    import torch
+
+    import synth
+
+    cfg = nv.KVConfig()
+    ring = nv.KVRing(cfg)
+    kb, vb = synth.kv_chunk(1005, 0, KV_T, KV_H, KV_D)
+    Ks = [bf16_from_bits(kb, dev) for _ in range(args.sets)]
+    Vs = [bf16_from_bits(vb, dev) for _ in range(args.sets)]
+    cap = 4 * KV_T + 2 * 3 * 880
+    Ko = torch.empty((cap, KV_H, KV_D), dtype=torch.bfloat16, device=dev)
+    Vo = torch.empty_like(Ko)
+    gathered = []
+
+    def one_pass():
+        nonlocal ring
+        ring = nv.KVRing(cfg)
+        n_tot = 0
+        for t in range(40):
+            if t % 10 == 0:
+                ring.begin_shot(t)
+            k, _ = ring.gather_window(t, Ko, Vo)
+            n_tot += k.shape[0]
+            ring.store_chunk(t, Ks[t % args.sets], Vs[t % args.sets])
+        return n_tot
+
+    n_tok = one_pass()
+    torch.cuda.synchronize()
+    steps = max(1, args.steps // 10)
+    ms, wall = time_steps(lambda i: one_pass(), steps, 1)
+    per_tok = KV_H * KV_D * 2 * (2 + 0.5625)
+    alg = n_tok * per_tok + 40 * kv_bytes_per_chunk()
+    return {"ms": ms, "wall_ms": wall, "gbs": alg / ms / 1e6, "tokens_gathered": n_tok,
+            "alg_bytes": alg}
+
+
+# --------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import nvfp4_bit_quantization_amd as nv
+
+    nv.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.workload != "kv_chunk":
+        fn = {"gemm_attn": run_gemm_attn, "ffn": run_ffn, "ring64s": run_ring64s,
+              "quant_act": run_quant_act}[args.workload]
+        r = fn(nv, args, dev)
+        r["kernels"] = {k: {"launches": v[0], "mean_ms": v[1]} for k, v in r.get("kernels", {}).items()}
+        print(json.dumps({"workload": args.workload, **r}))
+        return
+
+    step, _ = setup_kv_chunk(nv, args, dev)
+    ms, wall = time_steps(step, args.steps, args.warmup)
+    alg_step = 2 * kv_bytes_per_chunk()
+    gbs = alg_step / ms / 1e6
+    kt = kernel_times(nv, step, args.steps, args.warmup + args.steps)
+    dom = max(kt, key=lambda k: kt[k][0] * kt[k][1])
+    per_launch = {"kv_encode": kv_bytes_per_chunk(), "kv_gather": kv_bytes_per_chunk(),
+                  "kv_stats": 2 * KV_T * KV_H * KV_D * 2, "kv_finalize": KV_H * KV_D * 4 + 8}
+    k_ms = kt[dom][1]
+    achieved = per_launch[dom] / k_ms / 1e6
+    roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_for(dom, per_launch[dom]),
+            "alg_bytes_per_launch": per_launch[dom], "mean_launch_us": round(k_ms * 1e3, 2)}
+
+    out = {"metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic",
+           "config": {"workload": "kv_chunk_quant_dequant", "tokens": KV_T, "heads": KV_H,
+                      "head_dim": KV_D, "input_dtype": "bf16", "search": "4/6",
+                      "buffer_sets": args.sets, "alg_bytes_per_step": alg_step},
+           "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+           "wall_ms_per_step": round(wall, 5),
+           "kernels_us": {k: round(v[1] * 1e3, 2) for k, v in kt.items()},
+           "roofline": roof}
+
+    if not args.no_secondary:
+        sec = {}
+        g = run_gemm_attn(nv, argparse.Namespace(steps=20, warmup=5, sets=args.sets), dev)
+        sec["gemm_w4a4_7040x3072x3072_bf16"] = {
+            "TFLOP/s": round(g["tflops"], 1), "frac_mfma_peak": round(g["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
+            "kernel_TFLOP/s": round(g["kernel_tflops"], 1), "ms": round(g["ms"], 4),
+            "peak_TFLOP/s": MFMA_F16_PEAK_TFLOPS}
+        q = run_quant_act(nv, argparse.Namespace(steps=30, warmup=5, sets=args.sets), dev)
+        sec["quantize_act_7040x3072_bf16"] = {
+            "GB/s": round(q["gbs"], 1), "frac_hbm_peak": round(q["gbs"] / HBM_PEAK_GBS, 4),
+            "us": round(q["ms"] * 1e3, 2),
+            "kernels_us": {k: round(v[1] * 1e3, 2) for k, v in q["kernels"].items()}}
+        out["secondary"] = sec
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_kv()
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

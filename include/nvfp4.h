@@ -1,0 +1,271 @@
+/*
+ * nvfp4.h -- C ABI of libnvfp4, the NVFP4 data path of LongLive-2.0 on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library implements four things the LongLive-2.0 pages describe:
+ *   1. NVFP4 quantize / dequantize: E2M1 4-bit elements, one FP8 E4M3 scale
+ *      per 16-element block, one FP32 scale per tensor; 1-D (1x16) blocks for
+ *      activations, 2-D (16x16) blocks for weights; the adaptive "Four Over
+ *      Six" search that tries the block targets 6 and 4 and keeps the
+ *      encoding with the lower squared error.
+ *      ("MCISLAB DeepRead: LongLive2" summary, Method / NVFP4 training;
+ *      ngjoo.com audit of arXiv 2605.18739, claim on adaptive block scaling;
+ *      "LongLive-2.0: Infrastruttura Parallela NVFP4 per Video Lunghi",
+ *      section Addestramento NVFP4.)
+ *   2. The chunk-level KV-cache quantizer: keys K-smoothed, each chunk of
+ *      F_c frames quantized independently into a ring; storage falls from
+ *      4*T_c*H*d to (9/8)*T_c*H*d bytes.  (DeepRead summary, Method /
+ *      inference infrastructure, parallel KV quantization.)
+ *   3. The parallel gather-dequantizer of the attention window
+ *      K_eff(t) = A_g u A_s u KV[t-W, t), overlapping tokens removed, the
+ *      shot sink tracked by two scalar pointers and rebound on a prompt
+ *      switch.  (DeepRead summary, algorithm design / Multi-Shot Attention
+ *      Sink; Italian page, section Multi-Shot Attention Sink.)
+ *   4. The W4A4 GEMM on NVFP4 operands.  (DeepRead summary, inference
+ *      infrastructure / NVFP4 inference; Italian page, Inferenza W4A4 NVFP4.)
+ *
+ * Conventions (all entry points):
+ *   - Device pointers are HIP device memory owned by the caller; the library
+ *     never allocates or frees device memory.  Host structs are caller-owned.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls enqueue work on it and return without synchronising the host.
+ *   - Every argument is validated on the host before anything is enqueued;
+ *     on failure the call returns a negative nvfp4_status, enqueues nothing
+ *     and sets a thread-local message readable with nvfp4_last_error().
+ *     Numeric problems on the device are not reported (that would need a
+ *     synchronisation).
+ *   - Device pointers must be 16-byte aligned (NVFP4_EALIGN otherwise).
+ *   - Numerics: every result is bit-identical to the CPU oracle's definition
+ *     (codes, scales, dequantized values, gathered KV); GEMM outputs differ
+ *     from the exact fp64 product only by fp32 accumulation rounding.
+ *   - Domain: finite inputs whose tensor amax is 0 or >= 2^-100.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_ABI_VERSION 1
+
+typedef enum nvfp4_status {
+    NVFP4_OK = 0,
+    NVFP4_EINVAL = -1, /* bad argument value or NULL pointer            */
+    NVFP4_EALIGN = -2, /* device pointer not 16-byte aligned            */
+    NVFP4_ESHAPE = -3, /* shapes inconsistent or not multiples of 16    */
+    NVFP4_ENOSPC = -4, /* workspace / ring / output capacity too small  */
+    NVFP4_ESTATE = -5, /* KV ring used out of order                     */
+    NVFP4_EHIP = -6    /* the HIP runtime reported an error at launch   */
+} nvfp4_status;
+
+enum { NVFP4_DTYPE_F32 = 0, NVFP4_DTYPE_BF16 = 1 };
+enum { NVFP4_LAYOUT_1D = 0, NVFP4_LAYOUT_2D = 1 };
+enum { NVFP4_SEARCH_6 = 0, NVFP4_SEARCH_4O6 = 1 };
+
+/* Library ABI version (NVFP4_ABI_VERSION of the built library). */
+int nvfp4_abi_version(void);
+/* Static text for a status code. */
+const char *nvfp4_status_string(int status);
+/* Detail of the last failure on the calling thread ("" if none). */
+const char *nvfp4_last_error(void);
+
+/*
+ * A packed NVFP4 tensor of logical shape [rows, cols] (row-major).
+ *   codes : device, rows * cols / 2 bytes.  Byte j of row r holds column 2j
+ *           in bits 0..3 and column 2j+1 in bits 4..7.  A nibble is
+ *           s e1 e0 m (bit 3 = sign): E2M1 magnitudes {0,.5,1,1.5,2,3,4,6}.
+ *   scales: device, OCP E4M3FN bytes (bias 7, max 448, sign bit 0).
+ *           1-D: [rows, cols/16], block (r, j) = row r, columns 16j..16j+15.
+ *           2-D: [rows/16, cols/16], block (I, J) = the 16x16 tile.
+ *   s_dec : device, one float: the FP32 tensor decode scale.
+ *   cols % 16 == 0; for 2-D also rows % 16 == 0.
+ * Value of element (r, c): V(code) * RN(E4M3(scale) * s_dec).
+ */
+typedef struct nvfp4_tensor {
+    uint8_t *codes;
+    uint8_t *scales;
+    float *s_dec;
+    int64_t rows;
+    int64_t cols;
+    int32_t layout; /* NVFP4_LAYOUT_1D or NVFP4_LAYOUT_2D */
+    int32_t reserved;
+} nvfp4_tensor;
+
+/* Bytes of `codes` and `scales` for a tensor of that shape and layout. */
+size_t nvfp4_codes_bytes(int64_t rows, int64_t cols);
+size_t nvfp4_scales_bytes(int64_t rows, int64_t cols, int32_t layout);
+
+/*
+ * Workspace (device bytes) nvfp4_quantize needs for a tensor of that shape:
+ * per-workgroup amax partials.  Pure host function.
+ */
+size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols, int32_t layout);
+
+/*
+ * Quantize x (device, contiguous [out->rows, out->cols], dtype F32 or BF16)
+ * into `out` (DeepRead summary, Method / NVFP4 training: hierarchical
+ * scaling; 2-D for weights, 1-D for activations; scale search over 6 and 4).
+ *   Tensor scale: amax = max|x| (or *amax_in when amax_in != NULL, the value
+ *   a fused producer already computed; device pointer), s_enc =
+ *   RN(2688/amax), s_dec = RN(amax/2688); amax == 0 gives s_enc = s_dec = 1.
+ *   Per block, for each target c in {6, 4} (only 6 with NVFP4_SEARCH_6):
+ *   scale = E4M3(RN(RN(amax_b / c) * s_enc)) (saturating at 448), decode
+ *   scale S = RN(scale * s_dec), codes = E2M1(RN(x * RN(1/S))) (0 if S == 0),
+ *   error = sum of RN(x - V*S)^2 in a fixed order; target 4 is kept only if
+ *   its error is strictly lower.
+ * Workspace: device, >= nvfp4_quantize_workspace_bytes(); contents on entry
+ * are ignored.  Writes out->codes, out->scales and *out->s_dec.
+ */
+int nvfp4_quantize(const void *x, int32_t x_dtype, const nvfp4_tensor *out, int32_t search,
+                   const float *amax_in, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Dequantize `in` into y (device, contiguous [rows, cols], F32 or BF16):
+ * y = V(code) * RN(E4M3(scale) * s_dec), rounded to nearest-even for BF16.
+ */
+int nvfp4_dequantize(const nvfp4_tensor *in, void *y, int32_t y_dtype, void *stream);
+
+/*
+ * W4A4 GEMM (DeepRead summary, inference infrastructure: BF16 GEMMs replaced
+ * by FP4 GEMMs on NVFP4 weights and activations):
+ *   Y[m, n] = RN(RN(s_A * s_W) * sum_k A_hat[m, k] * W_hat[n, k])
+ * with A_hat = V * E4M3 scale (exact), likewise W_hat; fp32 accumulation.
+ *   a: 1-D layout, [M, K].   w: 2-D layout, [N, K] (rows = output features).
+ *   y: device, contiguous [M, N] in F32 or BF16 (nearest-even).
+ * K % 16 == 0, N % 16 == 0, any M >= 0.
+ */
+int nvfp4_gemm_w4a4(const nvfp4_tensor *a, const nvfp4_tensor *w, void *y, int32_t y_dtype,
+                    void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* KV-cache ring                                                              */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Shape of the streaming KV cache (DeepRead summary: chunk of F_c = 8 latent
+ * frames; 5B model: 880 tokens per frame, 24 heads of width 128; global sink
+ * A_g = first S_g frames, shot sink A_s = first S_s frames of the current
+ * shot, window of W chunks).  K and V of a chunk are bf16 [T_c, heads,
+ * head_dim], token-major, T_c = tokens_per_frame * frames_per_chunk.
+ */
+typedef struct nvfp4_kv_config {
+    int32_t tokens_per_frame;   /* L_f  (880) */
+    int32_t frames_per_chunk;   /* F_c  (8)   */
+    int32_t heads;              /* H    (24)  */
+    int32_t head_dim;           /* d    (128), multiple of 16 */
+    int32_t sink_frames_global; /* S_g  (3),  0 <= S_g <= F_c */
+    int32_t sink_frames_shot;   /* S_s  (3),  0 <= S_s <= F_c */
+    int32_t window_chunks;      /* W    (4),  1 <= W <= NVFP4_KV_MAX_WINDOW */
+    int32_t search;             /* NVFP4_SEARCH_6 or NVFP4_SEARCH_4O6 */
+} nvfp4_kv_config;
+
+#define NVFP4_KV_MAX_WINDOW 16
+
+/*
+ * Host-side ring state.  Allocate it yourself (it is plain data), set it up
+ * with nvfp4_kv_ring_init and treat every field as read-only.  The device
+ * memory it points at is caller-owned.  Layout of that memory: W chunk slots
+ * (chunk c lives in slot c mod W), then a global-sink region and a shot-sink
+ * region; each region holds packed K codes, K scales, V codes, V scales
+ * ((9/8) bytes per K+V element), the chunk's key mean mu[H*d] (fp32) and its
+ * two FP32 decode scales.  A ring must not be used from two host threads at
+ * once.
+ */
+typedef struct nvfp4_kv_ring {
+    nvfp4_kv_config cfg;
+    uint8_t *base;          /* device memory given to nvfp4_kv_ring_init */
+    uint64_t bytes;         /* its size */
+    int64_t chunk_tokens;   /* T_c */
+    int64_t hd;             /* heads * head_dim */
+    int64_t slot_bytes;     /* bytes of one chunk slot */
+    int64_t gsink_offset;   /* byte offset of the global-sink region */
+    int64_t ssink_offset;   /* byte offset of the shot-sink region */
+    int64_t next_chunk;     /* number of chunks stored so far */
+    int64_t g_end;          /* sink pointer 1: end of A_g (token index) */
+    int64_t s_start;        /* sink pointer 2: first token of the current shot */
+} nvfp4_kv_ring;
+
+/* Device bytes a ring of this configuration needs (pure host). */
+size_t nvfp4_kv_ring_bytes(const nvfp4_kv_config *cfg);
+/* Device workspace nvfp4_kv_store_chunk needs (pure host). */
+size_t nvfp4_kv_store_workspace_bytes(const nvfp4_kv_config *cfg);
+
+/*
+ * Set up `ring` over caller-owned device memory `dev_mem` of `bytes` bytes
+ * (>= nvfp4_kv_ring_bytes(cfg)).  No device work is enqueued.  The ring
+ * starts empty with chunk 0 as the first shot (s_start = 0).
+ */
+int nvfp4_kv_ring_init(nvfp4_kv_ring *ring, const nvfp4_kv_config *cfg, void *dev_mem,
+                       size_t bytes);
+
+/*
+ * Prompt switch: rebind the shot sink A_s to the chunk about to be generated
+ * (chunk_idx must equal ring->next_chunk).  Sets s_start = chunk_idx * T_c;
+ * the global sink and the history are untouched (DeepRead summary: a prompt
+ * switch rebinds A_s and keeps the global sink and history).  Host-only.
+ */
+int nvfp4_kv_begin_shot(nvfp4_kv_ring *ring, int64_t chunk_idx);
+
+/*
+ * Quantize chunk `chunk_idx` (must equal ring->next_chunk) into its ring
+ * slot (DeepRead summary: chunk-level KV quantization, keys K-smoothed).
+ *   K, V: device bf16 [T_c, H, d].
+ *   mu[h, c] = (float)(sum / T_c), the per-channel key sum taken in double
+ *   over 64-token tiles (each in token order, tiles in order); K_s =
+ *   RN(K - mu).  K_s and V are each quantized 1-D along (h, c) with one FP32
+ *   tensor scale per chunk.  Chunk 0 also fills the global-sink region and
+ *   the first chunk of a shot fills the shot-sink region (byte copies of the
+ *   leading sink tokens, written by the same kernel).  Advances next_chunk.
+ * Workspace: device, >= nvfp4_kv_store_workspace_bytes().
+ */
+int nvfp4_kv_store_chunk(nvfp4_kv_ring *ring, int64_t chunk_idx, const void *K_bf16,
+                         const void *V_bf16, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/*
+ * Number of tokens in K_eff(step) (step must equal ring->next_chunk: the
+ * step that generates chunk `step`).  K_eff(step) = (A_g u A_s u
+ * [max(0, step-W)*T_c, step*T_c)) n [0, step*T_c).  Pure host.
+ */
+int nvfp4_kv_effective_tokens(const nvfp4_kv_ring *ring, int64_t step, int64_t *n_tokens);
+
+/*
+ * Dequantize K_eff(step) into K_out / V_out (device bf16 [n, H, d],
+ * ascending token order, each token once): K_hat = bf16(RN(x_hat + mu)),
+ * V_hat = bf16(x_hat), x_hat = V(code) * RN(scale * s_dec) of the token's
+ * own chunk.  capacity_tokens below n gives NVFP4_ENOSPC.  *n_tokens (host)
+ * receives n.  One kernel launch.
+ */
+int nvfp4_gather_window(const nvfp4_kv_ring *ring, int64_t step, void *K_out, void *V_out,
+                        int64_t capacity_tokens, int64_t *n_tokens, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Kernel timing                                                              */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Turn kernel timing on (on != 0) or off.  While on, every kernel launch of
+ * the library is bracketed by two HIP events recorded on the launch's
+ * stream (HIP events are created on first use and reused; no device memory
+ * is allocated).  Process-wide; off by default.
+ */
+int nvfp4_profile_enable(int on);
+
+/*
+ * Wait for every recorded launch, then report per kernel name (sorted):
+ * names (cap entries of name_len bytes, NUL-terminated), launch counts and
+ * summed event-to-event milliseconds.  Clears the record.  Returns the number
+ * of distinct kernels (which may exceed cap), or NVFP4_EHIP.
+ */
+int nvfp4_profile_collect(char *names, int name_len, int64_t *launches, double *total_ms,
+                          int cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

@@ -1,0 +1,335 @@
+"""nvfp4_bit_quantization_amd -- Python binding of libnvfp4 (MI355X / gfx950).
+
+Argument marshalling only: every step of the NVFP4 path runs in the HIP
+kernels of libnvfp4.so, called through its C ABI (include/nvfp4.h).  PyTorch
+provides device memory and the current stream.  There is no CPU fallback: if
+the library is not built, or the device is not a GPU, the calls raise.
+
+Entry points mirror the C ABI:
+    quantize, dequantize, gemm_w4a4, KVRing (kv_ring_init, kv_begin_shot,
+    kv_store_chunk, kv_effective_tokens, gather_window)
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+LAYOUT_1D = 0
+LAYOUT_2D = 1
+SEARCH_6 = 0
+SEARCH_4O6 = 1
+KV_MAX_WINDOW = 16
+
+_STATUS = {0: "ok", -1: "EINVAL", -2: "EALIGN", -3: "ESHAPE", -4: "ENOSPC", -5: "ESTATE",
+           -6: "EHIP"}
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class CTensor(C.Structure):
+    _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("s_dec", C.c_void_p),
+                ("rows", C.c_int64), ("cols", C.c_int64), ("layout", C.c_int32),
+                ("reserved", C.c_int32)]
+
+
+class CKvConfig(C.Structure):
+    _fields_ = [("tokens_per_frame", C.c_int32), ("frames_per_chunk", C.c_int32),
+                ("heads", C.c_int32), ("head_dim", C.c_int32),
+                ("sink_frames_global", C.c_int32), ("sink_frames_shot", C.c_int32),
+                ("window_chunks", C.c_int32), ("search", C.c_int32)]
+
+
+class CKvRing(C.Structure):
+    _fields_ = [("cfg", CKvConfig), ("base", C.c_void_p), ("bytes", C.c_uint64),
+                ("chunk_tokens", C.c_int64), ("hd", C.c_int64), ("slot_bytes", C.c_int64),
+                ("gsink_offset", C.c_int64), ("ssink_offset", C.c_int64),
+                ("next_chunk", C.c_int64), ("g_end", C.c_int64), ("s_start", C.c_int64)]
+
+
+_lib = None
+
+_EXPORTS = {
+    "nvfp4_abi_version": ([], C.c_int),
+    "nvfp4_status_string": ([C.c_int], C.c_char_p),
+    "nvfp4_last_error": ([], C.c_char_p),
+    "nvfp4_codes_bytes": ([C.c_int64, C.c_int64], C.c_size_t),
+    "nvfp4_scales_bytes": ([C.c_int64, C.c_int64, C.c_int32], C.c_size_t),
+    "nvfp4_quantize_workspace_bytes": ([C.c_int64, C.c_int64, C.c_int32], C.c_size_t),
+    "nvfp4_quantize": ([C.c_void_p, C.c_int32, C.POINTER(CTensor), C.c_int32, C.c_void_p,
+                        C.c_void_p, C.c_size_t, C.c_void_p], C.c_int),
+    "nvfp4_dequantize": ([C.POINTER(CTensor), C.c_void_p, C.c_int32, C.c_void_p], C.c_int),
+    "nvfp4_gemm_w4a4": ([C.POINTER(CTensor), C.POINTER(CTensor), C.c_void_p, C.c_int32,
+                         C.c_void_p], C.c_int),
+    "nvfp4_kv_ring_bytes": ([C.POINTER(CKvConfig)], C.c_size_t),
+    "nvfp4_kv_store_workspace_bytes": ([C.POINTER(CKvConfig)], C.c_size_t),
+    "nvfp4_kv_ring_init": ([C.POINTER(CKvRing), C.POINTER(CKvConfig), C.c_void_p, C.c_size_t],
+                           C.c_int),
+    "nvfp4_kv_begin_shot": ([C.POINTER(CKvRing), C.c_int64], C.c_int),
+    "nvfp4_kv_store_chunk": ([C.POINTER(CKvRing), C.c_int64, C.c_void_p, C.c_void_p,
+                              C.c_void_p, C.c_size_t, C.c_void_p], C.c_int),
+    "nvfp4_kv_effective_tokens": ([C.POINTER(CKvRing), C.c_int64, C.POINTER(C.c_int64)],
+                                  C.c_int),
+    "nvfp4_gather_window": ([C.POINTER(CKvRing), C.c_int64, C.c_void_p, C.c_void_p, C.c_int64,
+                             C.POINTER(C.c_int64), C.c_void_p], C.c_int),
+    "nvfp4_profile_enable": ([C.c_int], C.c_int),
+    "nvfp4_profile_collect": ([C.c_char_p, C.c_int, C.c_void_p, C.c_void_p, C.c_int], C.c_int),
+}
+
+
+def lib():
+    """The loaded libnvfp4.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run python -m "
+                               "nvfp4_bit_quantization_amd.build")
+        L = C.CDLL(LIB_PATH)
+        for name, (args, res) in _EXPORTS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise NVFP4Error(status, lib().nvfp4_last_error().decode())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return C.c_void_p(t.data_ptr())
+
+
+_DT = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}
+
+
+# --------------------------------------------------------------------------
+# NVFP4 tensors
+# --------------------------------------------------------------------------
+
+@dataclass
+class NVFP4Tensor:
+    """Packed NVFP4 tensor on the GPU.
+
+    codes  uint8 [rows, cols/2]; scales uint8 (E4M3FN bytes) [rows, cols/16]
+    (1-D) or [rows/16, cols/16] (2-D); s_dec_bits int32 [1]: the raw bits of
+    the FP32 tensor decode scale, kept in an integer tensor so that a dtype
+    cast of a module cannot alter it.
+    """
+    codes: torch.Tensor
+    scales: torch.Tensor
+    s_dec_bits: torch.Tensor
+    rows: int
+    cols: int
+    layout: int
+
+    @staticmethod
+    def empty(rows: int, cols: int, layout: int = LAYOUT_1D, device="cuda") -> "NVFP4Tensor":
+        nsr = rows // 16 if layout == LAYOUT_2D else rows
+        return NVFP4Tensor(
+            codes=torch.empty((rows, cols // 2), dtype=torch.uint8, device=device),
+            scales=torch.empty((nsr, cols // 16), dtype=torch.uint8, device=device),
+            s_dec_bits=torch.empty(4, dtype=torch.int32, device=device),
+            rows=rows, cols=cols, layout=layout)
+
+    @property
+    def s_dec(self) -> float:
+        return float(self.s_dec_bits[:1].view(torch.float32).item())
+
+    def c(self) -> CTensor:
+        return CTensor(self.codes.data_ptr(), self.scales.data_ptr(), self.s_dec_bits.data_ptr(),
+                       self.rows, self.cols, self.layout, 0)
+
+
+def quantize_workspace_bytes(rows: int, cols: int, layout: int = LAYOUT_1D) -> int:
+    return int(lib().nvfp4_quantize_workspace_bytes(rows, cols, layout))
+
+
+def quantize(x: torch.Tensor, layout: int = LAYOUT_1D, search: int = SEARCH_4O6,
+             amax_in: torch.Tensor | None = None, out: NVFP4Tensor | None = None,
+             workspace: torch.Tensor | None = None, stream=None) -> NVFP4Tensor:
+    """nvfp4_quantize: x (GPU, float32 or bfloat16, [rows, cols]) -> NVFP4Tensor."""
+    if x.dim() != 2:
+        raise ValueError("quantize expects a 2-D tensor")
+    if x.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    rows, cols = x.shape
+    if out is None:
+        out = NVFP4Tensor.empty(rows, cols, layout, x.device)
+    if workspace is None and amax_in is None:
+        workspace = torch.empty(quantize_workspace_bytes(rows, cols, layout), dtype=torch.uint8,
+                                device=x.device)
+    ct = out.c()
+    _check(lib().nvfp4_quantize(
+        _dev(x, "x"), _DT[x.dtype], C.byref(ct), search,
+        C.c_void_p(amax_in.data_ptr()) if amax_in is not None else None,
+        C.c_void_p(workspace.data_ptr()) if workspace is not None else None,
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(stream)))
+    return out
+
+
+def dequantize(t: NVFP4Tensor, dtype=torch.bfloat16, out: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+    """nvfp4_dequantize: NVFP4Tensor -> [rows, cols] float32 or bfloat16."""
+    if out is None:
+        out = torch.empty((t.rows, t.cols), dtype=dtype, device=t.codes.device)
+    ct = t.c()
+    _check(lib().nvfp4_dequantize(C.byref(ct), _dev(out, "out"), _DT[out.dtype],
+                                  _stream(stream)))
+    return out
+
+
+def gemm_w4a4(a: NVFP4Tensor, w: NVFP4Tensor, out_dtype=torch.bfloat16,
+              out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """nvfp4_gemm_w4a4: Y[M, N] = s_A s_W A_hat W_hat^T (A 1-D, W 2-D)."""
+    if out is None:
+        out = torch.empty((a.rows, w.rows), dtype=out_dtype, device=a.codes.device)
+    ca, cw = a.c(), w.c()
+    _check(lib().nvfp4_gemm_w4a4(C.byref(ca), C.byref(cw), _dev(out, "out"), _DT[out.dtype],
+                                 _stream(stream)))
+    return out
+
+
+# --------------------------------------------------------------------------
+# KV ring
+# --------------------------------------------------------------------------
+
+@dataclass
+class KVConfig:
+    tokens_per_frame: int = 880
+    frames_per_chunk: int = 8
+    heads: int = 24
+    head_dim: int = 128
+    sink_frames_global: int = 3
+    sink_frames_shot: int = 3
+    window_chunks: int = 4
+    search: int = SEARCH_4O6
+
+    def c(self) -> CKvConfig:
+        return CKvConfig(self.tokens_per_frame, self.frames_per_chunk, self.heads, self.head_dim,
+                         self.sink_frames_global, self.sink_frames_shot, self.window_chunks,
+                         self.search)
+
+    @property
+    def chunk_tokens(self) -> int:
+        return self.tokens_per_frame * self.frames_per_chunk
+
+
+def kv_ring_bytes(cfg: KVConfig) -> int:
+    c = cfg.c()
+    return int(lib().nvfp4_kv_ring_bytes(C.byref(c)))
+
+
+def kv_store_workspace_bytes(cfg: KVConfig) -> int:
+    c = cfg.c()
+    return int(lib().nvfp4_kv_store_workspace_bytes(C.byref(c)))
+
+
+class KVRing:
+    """Streaming NVFP4 KV cache: W chunk slots plus global and shot sink copies.
+
+    Device memory comes from torch (uint8 tensors) and is owned by this
+    object; the ring state is the C struct nvfp4_kv_ring.
+    """
+
+    def __init__(self, cfg: KVConfig, device="cuda"):
+        self.cfg = cfg
+        c = cfg.c()
+        nbytes = int(lib().nvfp4_kv_ring_bytes(C.byref(c)))
+        if nbytes == 0:
+            _check(lib().nvfp4_kv_ring_init(None, C.byref(c), None, 0))
+        self.mem = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        off = (-self.mem.data_ptr()) % 256
+        self._base = self.mem.data_ptr() + off
+        self.ws = torch.empty(kv_store_workspace_bytes(cfg) + 256, dtype=torch.uint8,
+                              device=device)
+        self.ring = CKvRing()
+        _check(lib().nvfp4_kv_ring_init(C.byref(self.ring), C.byref(c), C.c_void_p(self._base),
+                                        nbytes))
+
+    @property
+    def next_chunk(self) -> int:
+        return int(self.ring.next_chunk)
+
+    def begin_shot(self, chunk_idx: int):
+        _check(lib().nvfp4_kv_begin_shot(C.byref(self.ring), chunk_idx))
+
+    def store_chunk(self, chunk_idx: int, K: torch.Tensor, V: torch.Tensor, stream=None):
+        if K.dtype != torch.bfloat16 or V.dtype != torch.bfloat16:
+            raise ValueError("K and V must be bfloat16")
+        T, hd = self.cfg.chunk_tokens, self.cfg.heads * self.cfg.head_dim
+        if K.numel() != T * hd or V.numel() != T * hd:
+            raise ValueError(f"K and V must hold [{T}, {self.cfg.heads}, {self.cfg.head_dim}]")
+        _check(lib().nvfp4_kv_store_chunk(C.byref(self.ring), chunk_idx, _dev(K, "K"),
+                                          _dev(V, "V"), C.c_void_p(self.ws.data_ptr()),
+                                          self.ws.numel(), _stream(stream)))
+
+    def effective_tokens(self, step: int) -> int:
+        n = C.c_int64()
+        _check(lib().nvfp4_kv_effective_tokens(C.byref(self.ring), step, C.byref(n)))
+        return int(n.value)
+
+    def gather_window(self, step: int, K_out: torch.Tensor | None = None,
+                      V_out: torch.Tensor | None = None, stream=None):
+        """Dequantized K_eff(step), V_eff(step): bf16 [n, heads, head_dim]."""
+        n = self.effective_tokens(step)
+        shape = (n, self.cfg.heads, self.cfg.head_dim)
+        dev = self.mem.device
+        if K_out is None:
+            K_out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        if V_out is None:
+            V_out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        cap = min(K_out.shape[0], V_out.shape[0]) if K_out.dim() else 0
+        got = C.c_int64()
+        _check(lib().nvfp4_gather_window(C.byref(self.ring), step, _dev(K_out, "K_out"),
+                                         _dev(V_out, "V_out"), cap, C.byref(got),
+                                         _stream(stream)))
+        return K_out[:got.value], V_out[:got.value]
+
+
+# --------------------------------------------------------------------------
+# Kernel timing
+# --------------------------------------------------------------------------
+
+def profile_enable(on: bool = True):
+    """nvfp4_profile_enable: bracket every library kernel launch with HIP events."""
+    _check(lib().nvfp4_profile_enable(1 if on else 0))
+
+
+def profile_collect(cap: int = 64) -> dict:
+    """nvfp4_profile_collect: {kernel name: (launches, total ms)}; clears the record."""
+    name_len = 64
+    names = C.create_string_buffer(cap * name_len)
+    launches = (C.c_int64 * cap)()
+    total = (C.c_double * cap)()
+    n = lib().nvfp4_profile_collect(names, name_len, launches, total, cap)
+    if n < 0:
+        _check(n)
+    out = {}
+    for i in range(min(n, cap)):
+        nm = names.raw[i * name_len:(i + 1) * name_len].split(b"\0", 1)[0].decode()
+        out[nm] = (int(launches[i]), float(total[i]))
+    return out

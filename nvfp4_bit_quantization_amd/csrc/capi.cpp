@@ -1,0 +1,410 @@
+// capi.cpp -- the C ABI of libnvfp4 (declared in include/nvfp4.h).
+//
+// Host side only: argument validation (before anything is enqueued), ring
+// bookkeeping of the multi-shot sink's two scalar pointers, planning of the
+// effective set, and kernel launches on the caller's stream.  No call
+// allocates device memory or synchronises the host.
+#include "../../include/nvfp4.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return NVFP4_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int64_t align256(int64_t b) { return (b + 255) & ~(int64_t)255; }
+
+int check_tensor(const nvfp4_tensor *t, const char *name) {
+    if (!t) return fail(NVFP4_EINVAL, "%s: NULL tensor", name);
+    if (t->layout != NVFP4_LAYOUT_1D && t->layout != NVFP4_LAYOUT_2D)
+        return fail(NVFP4_EINVAL, "%s: layout %d is neither 1-D nor 2-D", name, t->layout);
+    if (t->rows < 0 || t->cols < 0)
+        return fail(NVFP4_ESHAPE, "%s: negative shape [%lld, %lld]", name, (long long)t->rows,
+                    (long long)t->cols);
+    if (t->cols % 16)
+        return fail(NVFP4_ESHAPE, "%s: cols %lld not a multiple of 16", name, (long long)t->cols);
+    if (t->layout == NVFP4_LAYOUT_2D && t->rows % 16)
+        return fail(NVFP4_ESHAPE, "%s: 2-D layout needs rows %% 16 == 0, got %lld", name,
+                    (long long)t->rows);
+    if (!t->s_dec) return fail(NVFP4_EINVAL, "%s: NULL s_dec", name);
+    if (t->rows * t->cols > 0 && (!t->codes || !t->scales))
+        return fail(NVFP4_EINVAL, "%s: NULL codes or scales", name);
+    if (!aligned16(t->codes) || !aligned16(t->scales) || ((uintptr_t)t->s_dec & 3u))
+        return fail(NVFP4_EALIGN, "%s: codes/scales must be 16-byte aligned", name);
+    return NVFP4_OK;
+}
+
+int hip_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(NVFP4_EHIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+// ---- KV ring layout ---------------------------------------------------------
+
+struct RegionLayout {
+    int64_t kc, ks, vc, vs, mu, sd, bytes;
+};
+
+RegionLayout region_layout(int64_t tokens, int64_t hd) {
+    RegionLayout r;
+    int64_t o = 0;
+    r.kc = o;
+    o += align256(tokens * hd / 2);
+    r.ks = o;
+    o += align256(tokens * hd / 16);
+    r.vc = o;
+    o += align256(tokens * hd / 2);
+    r.vs = o;
+    o += align256(tokens * hd / 16);
+    r.mu = o;
+    o += align256(hd * 4);
+    r.sd = o;
+    o += 256;
+    r.bytes = o;
+    return r;
+}
+
+int check_kv_config(const nvfp4_kv_config *c) {
+    if (!c) return fail(NVFP4_EINVAL, "NULL kv config");
+    if (c->tokens_per_frame < 1 || c->frames_per_chunk < 1 || c->heads < 1 || c->head_dim < 16)
+        return fail(NVFP4_EINVAL, "kv config: sizes must be positive (head_dim >= 16)");
+    if (c->head_dim % 16) return fail(NVFP4_ESHAPE, "kv config: head_dim %% 16 != 0");
+    if (c->sink_frames_global < 0 || c->sink_frames_global > c->frames_per_chunk ||
+        c->sink_frames_shot < 0 || c->sink_frames_shot > c->frames_per_chunk)
+        return fail(NVFP4_EINVAL, "kv config: sink frames must lie in [0, frames_per_chunk]");
+    if (c->window_chunks < 1 || c->window_chunks > NVFP4_KV_MAX_WINDOW)
+        return fail(NVFP4_EINVAL, "kv config: window_chunks must lie in [1, %d]",
+                    NVFP4_KV_MAX_WINDOW);
+    if (c->search != NVFP4_SEARCH_6 && c->search != NVFP4_SEARCH_4O6)
+        return fail(NVFP4_EINVAL, "kv config: bad search %d", c->search);
+    const int64_t T = (int64_t)c->tokens_per_frame * c->frames_per_chunk;
+    const int64_t hd = (int64_t)c->heads * c->head_dim;
+    if (T * hd >= ((int64_t)1 << 31))
+        return fail(NVFP4_ESHAPE, "kv config: a chunk of %lld elements is too large",
+                    (long long)(T * hd));
+    return NVFP4_OK;
+}
+
+nvfp4::KvRegion region_at(uint8_t *base, const RegionLayout &L) {
+    nvfp4::KvRegion r;
+    r.kc = base + L.kc;
+    r.ks = base + L.ks;
+    r.vc = base + L.vc;
+    r.vs = base + L.vs;
+    r.mu = (float *)(base + L.mu);
+    r.sd = (float *)(base + L.sd);
+    return r;
+}
+
+struct Plan {
+    int64_t n_g, n_s, c_lo, nwin, total;
+};
+
+// K_eff(t) = (A_g u A_s u [max(0, t-W)*Tc, t*Tc)) n [0, t*Tc): the sinks lie
+// at the start of their chunks, so a sink either sits inside the window
+// (served from the ring slot) or entirely below it (served from its copy).
+Plan plan_effective(const nvfp4_kv_ring *r, int64_t t) {
+    const int64_t Tc = r->chunk_tokens, W = r->cfg.window_chunks;
+    Plan p;
+    p.c_lo = t - W > 0 ? t - W : 0;
+    p.nwin = t - p.c_lo;
+    const int64_t win_lo = p.c_lo * Tc, hi = t * Tc;
+    const int64_t g_end = r->g_end < hi ? r->g_end : hi;
+    // global sink part below the window
+    p.n_g = 0;
+    if (g_end > 0 && win_lo > 0) p.n_g = g_end < win_lo ? g_end : win_lo;
+    // shot sink part below the window, minus overlap with the global sink
+    p.n_s = 0;
+    const int64_t s_lo = r->s_start;
+    int64_t s_hi = r->s_start + (int64_t)r->cfg.sink_frames_shot * r->cfg.tokens_per_frame;
+    if (s_hi > hi) s_hi = hi;
+    if (s_hi > win_lo) s_hi = win_lo;
+    int64_t lo = s_lo > p.n_g ? s_lo : p.n_g;
+    if (s_hi > lo) p.n_s = s_hi - lo;
+    p.total = p.n_g + p.n_s + p.nwin * Tc;
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
+
+const char *nvfp4_status_string(int status) {
+    switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_EINVAL: return "invalid argument";
+    case NVFP4_EALIGN: return "misaligned device pointer";
+    case NVFP4_ESHAPE: return "bad shape";
+    case NVFP4_ENOSPC: return "buffer too small";
+    case NVFP4_ESTATE: return "KV ring used out of order";
+    case NVFP4_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+const char *nvfp4_last_error(void) { return g_err; }
+
+size_t nvfp4_codes_bytes(int64_t rows, int64_t cols) {
+    return (rows < 0 || cols < 0) ? 0 : (size_t)(rows * cols / 2);
+}
+
+size_t nvfp4_scales_bytes(int64_t rows, int64_t cols, int32_t layout) {
+    if (rows < 0 || cols < 0) return 0;
+    return layout == NVFP4_LAYOUT_2D ? (size_t)((rows / 16) * (cols / 16))
+                                     : (size_t)(rows * (cols / 16));
+}
+
+size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols, int32_t layout) {
+    (void)layout;
+    if (rows < 0 || cols < 0) return 0;
+    return (size_t)nvfp4::kMaxPartials * sizeof(float);
+}
+
+int nvfp4_quantize(const void *x, int32_t x_dtype, const nvfp4_tensor *out, int32_t search,
+                   const float *amax_in, void *workspace, size_t workspace_bytes,
+                   void *stream) {
+    int st = check_tensor(out, "quantize out");
+    if (st) return st;
+    if (x_dtype != NVFP4_DTYPE_F32 && x_dtype != NVFP4_DTYPE_BF16)
+        return fail(NVFP4_EINVAL, "quantize: bad x dtype %d", x_dtype);
+    if (search != NVFP4_SEARCH_6 && search != NVFP4_SEARCH_4O6)
+        return fail(NVFP4_EINVAL, "quantize: bad search %d", search);
+    const int64_t n = out->rows * out->cols;
+    if (n > 0 && !x) return fail(NVFP4_EINVAL, "quantize: NULL x");
+    if (!aligned16(x)) return fail(NVFP4_EALIGN, "quantize: x not 16-byte aligned");
+    if (((uintptr_t)amax_in & 3u)) return fail(NVFP4_EALIGN, "quantize: amax_in misaligned");
+    const size_t need = nvfp4_quantize_workspace_bytes(out->rows, out->cols, out->layout);
+    if (!amax_in && (!workspace || workspace_bytes < need))
+        return fail(NVFP4_ENOSPC, "quantize: workspace %zu < %zu bytes", workspace_bytes, need);
+    if (!aligned16(workspace)) return fail(NVFP4_EALIGN, "quantize: workspace misaligned");
+    hipStream_t s = (hipStream_t)stream;
+    float *partials = (float *)workspace;
+    int np = 0;
+    if (!amax_in) {
+        np = nvfp4::amax_partials_for(n);
+        hipError_t e = nvfp4::launch_amax(x, x_dtype, n, partials, np, s);
+        if (e != hipSuccess) return hip_status(e, "quantize amax launch");
+    }
+    hipError_t e = nvfp4::launch_encode(x, x_dtype, out->rows, out->cols, out->layout, search,
+                                        partials, np, amax_in, out->codes, out->scales,
+                                        out->s_dec, s);
+    return hip_status(e, "quantize encode launch");
+}
+
+int nvfp4_dequantize(const nvfp4_tensor *in, void *y, int32_t y_dtype, void *stream) {
+    int st = check_tensor(in, "dequantize in");
+    if (st) return st;
+    if (y_dtype != NVFP4_DTYPE_F32 && y_dtype != NVFP4_DTYPE_BF16)
+        return fail(NVFP4_EINVAL, "dequantize: bad y dtype %d", y_dtype);
+    const int64_t n = in->rows * in->cols;
+    if (n > 0 && !y) return fail(NVFP4_EINVAL, "dequantize: NULL y");
+    if (!aligned16(y)) return fail(NVFP4_EALIGN, "dequantize: y not 16-byte aligned");
+    if (n == 0) return ok();
+    hipError_t e = nvfp4::launch_dequant(in->codes, in->scales, in->s_dec, in->rows, in->cols,
+                                         in->layout, y, y_dtype, (hipStream_t)stream);
+    return hip_status(e, "dequantize launch");
+}
+
+int nvfp4_gemm_w4a4(const nvfp4_tensor *a, const nvfp4_tensor *w, void *y, int32_t y_dtype,
+                    void *stream) {
+    int st = check_tensor(a, "gemm A");
+    if (st) return st;
+    st = check_tensor(w, "gemm W");
+    if (st) return st;
+    if (a->layout != NVFP4_LAYOUT_1D)
+        return fail(NVFP4_EINVAL, "gemm: A must use 1-D (1x16) block scaling");
+    if (w->layout != NVFP4_LAYOUT_2D)
+        return fail(NVFP4_EINVAL, "gemm: W must use 2-D (16x16) block scaling");
+    if (a->cols != w->cols)
+        return fail(NVFP4_ESHAPE, "gemm: K mismatch (A has %lld, W has %lld)",
+                    (long long)a->cols, (long long)w->cols);
+    if (y_dtype != NVFP4_DTYPE_F32 && y_dtype != NVFP4_DTYPE_BF16)
+        return fail(NVFP4_EINVAL, "gemm: bad y dtype %d", y_dtype);
+    if (a->rows * w->rows > 0 && !y) return fail(NVFP4_EINVAL, "gemm: NULL y");
+    if (!aligned16(y)) return fail(NVFP4_EALIGN, "gemm: y not 16-byte aligned");
+    hipError_t e = nvfp4::launch_gemm_w4a4(a->codes, a->scales, a->s_dec, w->codes, w->scales,
+                                           w->s_dec, a->rows, w->rows, a->cols, y, y_dtype,
+                                           (hipStream_t)stream);
+    return hip_status(e, "gemm launch");
+}
+
+// ---- KV ring ------------------------------------------------------------------
+
+size_t nvfp4_kv_ring_bytes(const nvfp4_kv_config *cfg) {
+    if (check_kv_config(cfg)) return 0;
+    const int64_t T = (int64_t)cfg->tokens_per_frame * cfg->frames_per_chunk;
+    const int64_t hd = (int64_t)cfg->heads * cfg->head_dim;
+    const int64_t g = (int64_t)cfg->sink_frames_global * cfg->tokens_per_frame;
+    const int64_t sh = (int64_t)cfg->sink_frames_shot * cfg->tokens_per_frame;
+    return (size_t)(cfg->window_chunks * region_layout(T, hd).bytes +
+                    region_layout(g, hd).bytes + region_layout(sh, hd).bytes);
+}
+
+size_t nvfp4_kv_store_workspace_bytes(const nvfp4_kv_config *cfg) {
+    if (check_kv_config(cfg)) return 0;
+    const int64_t T = (int64_t)cfg->tokens_per_frame * cfg->frames_per_chunk;
+    const int64_t hd = (int64_t)cfg->heads * cfg->head_dim;
+    return nvfp4::kv_store_ws_bytes(T, hd);
+}
+
+int nvfp4_kv_ring_init(nvfp4_kv_ring *ring, const nvfp4_kv_config *cfg, void *dev_mem,
+                       size_t bytes) {
+    if (!ring) return fail(NVFP4_EINVAL, "kv_ring_init: NULL ring");
+    int st = check_kv_config(cfg);
+    if (st) return st;
+    if (!dev_mem) return fail(NVFP4_EINVAL, "kv_ring_init: NULL device memory");
+    if (((uintptr_t)dev_mem & 255u))
+        return fail(NVFP4_EALIGN, "kv_ring_init: device memory must be 256-byte aligned");
+    const size_t need = nvfp4_kv_ring_bytes(cfg);
+    if (bytes < need) return fail(NVFP4_ENOSPC, "kv_ring_init: %zu < %zu bytes", bytes, need);
+    memset(ring, 0, sizeof(*ring));
+    ring->cfg = *cfg;
+    ring->base = (uint8_t *)dev_mem;
+    ring->bytes = bytes;
+    ring->chunk_tokens = (int64_t)cfg->tokens_per_frame * cfg->frames_per_chunk;
+    ring->hd = (int64_t)cfg->heads * cfg->head_dim;
+    ring->slot_bytes = region_layout(ring->chunk_tokens, ring->hd).bytes;
+    ring->gsink_offset = cfg->window_chunks * ring->slot_bytes;
+    ring->ssink_offset =
+        ring->gsink_offset +
+        region_layout((int64_t)cfg->sink_frames_global * cfg->tokens_per_frame, ring->hd).bytes;
+    ring->next_chunk = 0;
+    ring->g_end = (int64_t)cfg->sink_frames_global * cfg->tokens_per_frame;
+    ring->s_start = 0;
+    return ok();
+}
+
+static int check_ring(const nvfp4_kv_ring *r) {
+    if (!r || !r->base) return fail(NVFP4_EINVAL, "NULL or uninitialised ring");
+    return check_kv_config(&r->cfg);
+}
+
+int nvfp4_kv_begin_shot(nvfp4_kv_ring *ring, int64_t chunk_idx) {
+    int st = check_ring(ring);
+    if (st) return st;
+    if (chunk_idx != ring->next_chunk)
+        return fail(NVFP4_ESTATE, "kv_begin_shot: chunk %lld is not the next chunk (%lld)",
+                    (long long)chunk_idx, (long long)ring->next_chunk);
+    ring->s_start = chunk_idx * ring->chunk_tokens;
+    return ok();
+}
+
+int nvfp4_kv_store_chunk(nvfp4_kv_ring *ring, int64_t chunk_idx, const void *K_bf16,
+                         const void *V_bf16, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+    int st = check_ring(ring);
+    if (st) return st;
+    if (chunk_idx != ring->next_chunk)
+        return fail(NVFP4_ESTATE, "kv_store_chunk: chunk %lld stored out of order (next %lld)",
+                    (long long)chunk_idx, (long long)ring->next_chunk);
+    if (!K_bf16 || !V_bf16) return fail(NVFP4_EINVAL, "kv_store_chunk: NULL K or V");
+    if (!aligned16(K_bf16) || !aligned16(V_bf16) || !aligned16(workspace))
+        return fail(NVFP4_EALIGN, "kv_store_chunk: K, V and workspace must be 16-byte aligned");
+    const size_t need = nvfp4_kv_store_workspace_bytes(&ring->cfg);
+    if (!workspace || workspace_bytes < need)
+        return fail(NVFP4_ENOSPC, "kv_store_chunk: workspace %zu < %zu bytes", workspace_bytes,
+                    need);
+    const nvfp4_kv_config &c = ring->cfg;
+    const int64_t T = ring->chunk_tokens, hd = ring->hd;
+    const int64_t gtok = (int64_t)c.sink_frames_global * c.tokens_per_frame;
+    const int64_t stok = (int64_t)c.sink_frames_shot * c.tokens_per_frame;
+    nvfp4::KvStoreArgs a;
+    a.K = (const uint16_t *)K_bf16;
+    a.V = (const uint16_t *)V_bf16;
+    a.T = T;
+    a.HD = hd;
+    a.search = c.search;
+    a.slot = region_at(ring->base + (chunk_idx % c.window_chunks) * ring->slot_bytes,
+                       region_layout(T, hd));
+    a.gsink = region_at(ring->base + ring->gsink_offset, region_layout(gtok, hd));
+    a.ssink = region_at(ring->base + ring->ssink_offset, region_layout(stok, hd));
+    a.g_tokens = (chunk_idx == 0) ? gtok : 0;
+    a.s_tokens = (chunk_idx * T == ring->s_start) ? stok : 0;
+    a.ws = workspace;
+    hipError_t e = nvfp4::launch_kv_store(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "kv_store_chunk launch");
+    ring->next_chunk = chunk_idx + 1;
+    return ok();
+}
+
+int nvfp4_kv_effective_tokens(const nvfp4_kv_ring *ring, int64_t step, int64_t *n_tokens) {
+    int st = check_ring(ring);
+    if (st) return st;
+    if (!n_tokens) return fail(NVFP4_EINVAL, "kv_effective_tokens: NULL n_tokens");
+    if (step != ring->next_chunk)
+        return fail(NVFP4_ESTATE, "kv_effective_tokens: step %lld != next chunk %lld",
+                    (long long)step, (long long)ring->next_chunk);
+    *n_tokens = plan_effective(ring, step).total;
+    return ok();
+}
+
+int nvfp4_gather_window(const nvfp4_kv_ring *ring, int64_t step, void *K_out, void *V_out,
+                        int64_t capacity_tokens, int64_t *n_tokens, void *stream) {
+    int st = check_ring(ring);
+    if (st) return st;
+    if (step != ring->next_chunk)
+        return fail(NVFP4_ESTATE, "gather_window: step %lld != next chunk %lld",
+                    (long long)step, (long long)ring->next_chunk);
+    const Plan p = plan_effective(ring, step);
+    if (n_tokens) *n_tokens = p.total;
+    if (p.total > capacity_tokens)
+        return fail(NVFP4_ENOSPC, "gather_window: %lld tokens exceed capacity %lld",
+                    (long long)p.total, (long long)capacity_tokens);
+    if (p.total > 0 && (!K_out || !V_out)) return fail(NVFP4_EINVAL, "gather_window: NULL output");
+    if (!aligned16(K_out) || !aligned16(V_out))
+        return fail(NVFP4_EALIGN, "gather_window: outputs must be 16-byte aligned");
+    const nvfp4_kv_config &c = ring->cfg;
+    const int64_t T = ring->chunk_tokens, hd = ring->hd;
+    nvfp4::GatherArgs a;
+    a.gsink = region_at(ring->base + ring->gsink_offset,
+                        region_layout((int64_t)c.sink_frames_global * c.tokens_per_frame, hd));
+    a.ssink = region_at(ring->base + ring->ssink_offset,
+                        region_layout((int64_t)c.sink_frames_shot * c.tokens_per_frame, hd));
+    a.slot0 = region_at(ring->base, region_layout(T, hd));
+    a.slot_bytes = ring->slot_bytes;
+    a.n_g = p.n_g;
+    a.n_s = p.n_s;
+    a.c_lo = p.c_lo;
+    a.Tc = T;
+    a.W = c.window_chunks;
+    a.n_tokens = p.total;
+    a.HD = hd;
+    a.Kout = (uint16_t *)K_out;
+    a.Vout = (uint16_t *)V_out;
+    // the shot-sink copy starts at the shot's first token; skip the part
+    // already served by the global sink
+    if (p.n_s > 0) {
+        const int64_t skip = (ring->s_start > p.n_g ? ring->s_start : p.n_g) - ring->s_start;
+        a.ssink.kc += skip * hd / 2;
+        a.ssink.ks += skip * hd / 16;
+        a.ssink.vc += skip * hd / 2;
+        a.ssink.vs += skip * hd / 16;
+    }
+    hipError_t e = nvfp4::launch_gather(a, (hipStream_t)stream);
+    return hip_status(e, "gather_window launch");
+}
+
+}  // extern "C"

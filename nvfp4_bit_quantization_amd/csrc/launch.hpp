@@ -1,0 +1,93 @@
+// launch.hpp -- host-side launchers of the libnvfp4 kernels (internal).
+// Arguments are validated by the C ABI layer (capi.cpp) before these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// ---- profile.cpp: optional HIP-event timing of every launch
+bool prof_on();
+int prof_begin(const char *name, hipStream_t s);
+void prof_end(int idx, hipStream_t s);
+
+// Launch KERNEL (parenthesise template kernels) and, when timing is enabled,
+// bracket it with events recorded on the same stream under NAME.
+#define NVFP4_LAUNCH(NAME, KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)               \
+    do {                                                                         \
+        const bool _p = ::nvfp4::prof_on();                                      \
+        const int _i = _p ? ::nvfp4::prof_begin(NAME, STREAM) : -1;             \
+        hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);     \
+        if (_p) ::nvfp4::prof_end(_i, STREAM);                                   \
+    } while (0)
+
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+constexpr int kMaxPartials = 2048;  // amax partials per quantize call
+
+// ---- quantize.hip
+int amax_partials_for(int64_t n);
+hipError_t launch_amax(const void *x, int dtype, int64_t n, float *partials, int np,
+                       hipStream_t s);
+hipError_t launch_encode(const void *x, int dtype, int64_t rows, int64_t cols, int layout,
+                         int search, const float *partials, int np, const float *amax_in,
+                         uint8_t *codes, uint8_t *scales, float *s_dec, hipStream_t s);
+hipError_t launch_dequant(const uint8_t *codes, const uint8_t *scales, const float *s_dec,
+                          int64_t rows, int64_t cols, int layout, void *y, int ydtype,
+                          hipStream_t s);
+
+// ---- kv.hip
+// Addresses of one ring region (a chunk slot or a sink copy).
+struct KvRegion {
+    uint8_t *kc;  // K codes   [tokens, HD/2]
+    uint8_t *ks;  // K scales  [tokens, HD/16]
+    uint8_t *vc;  // V codes
+    uint8_t *vs;  // V scales
+    float *mu;    // [HD]
+    float *sd;    // [2]: s_dec of K_s, s_dec of V
+};
+
+struct KvStoreArgs {
+    const uint16_t *K;
+    const uint16_t *V;
+    int64_t T;   // tokens in the chunk
+    int64_t HD;  // heads * head_dim
+    int search;
+    KvRegion slot;
+    KvRegion gsink;  // written when g_tokens > 0
+    KvRegion ssink;  // written when s_tokens > 0
+    int64_t g_tokens;
+    int64_t s_tokens;
+    void *ws;
+};
+size_t kv_store_ws_bytes(int64_t T, int64_t HD);
+hipError_t launch_kv_store(const KvStoreArgs &a, hipStream_t s);
+
+// Gather plan of K_eff(t): n_g tokens from the global-sink copy, then n_s
+// tokens from the shot-sink copy (both only when outside the window), then
+// the window chunks c_lo, c_lo+1, ... (chunk c in slot c mod W).
+struct GatherArgs {
+    KvRegion gsink;
+    KvRegion ssink;
+    KvRegion slot0;      // slot 0; slot k is slot0 + k * slot_bytes
+    int64_t slot_bytes;
+    int64_t n_g;
+    int64_t n_s;
+    int64_t c_lo;
+    int64_t Tc;
+    int64_t W;
+    int64_t n_tokens;
+    int64_t HD;
+    uint16_t *Kout;
+    uint16_t *Vout;
+};
+hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
+
+// ---- gemm.hip
+hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_sdec,
+                            const uint8_t *w_codes, const uint8_t *w_scales,
+                            const float *w_sdec, int64_t M, int64_t N, int64_t K, void *y,
+                            int ydtype, hipStream_t s);
+
+}  // namespace nvfp4

@@ -1,0 +1,150 @@
+"""GPU parity: KV-cache chunk store and window gather vs the CPU oracle.
+
+Bar: ring contents (codes, scales, mu, s_dec) and gathered bf16 K/V bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import nvfp4_bit_quantization_amd as m
+
+    m.lib()
+    return m
+
+
+def chunk_inputs(seed, c, T, H, d):
+    kb, vb = synth.kv_chunk(seed, c, T, H, d)
+    Kg = torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16).cuda()
+    Vg = torch.from_numpy(vb.view(np.int16)).view(torch.bfloat16).cuda()
+    K = synth.bf16_bits_to_f32(kb).reshape(T, H * d)
+    V = synth.bf16_bits_to_f32(vb).reshape(T, H * d)
+    return Kg, Vg, K, V
+
+
+def bf16_np(t):
+    return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16).reshape(t.shape[0], -1)
+
+
+def run_ring(nv, orc, cfg, cuts, steps, seed, full_check=True, sample_tokens=None):
+    ring = nv.KVRing(cfg)
+    Tc, H, d = cfg.chunk_tokens, cfg.heads, cfg.head_dim
+    g_tok = cfg.sink_frames_global * cfg.tokens_per_frame
+    s_tok = cfg.sink_frames_shot * cfg.tokens_per_frame
+    chunks = {}
+    shot = 0
+    for t in range(steps):
+        if t in cuts:
+            shot = t
+            ring.begin_shot(t)
+        # gather of step t, then store chunk t
+        Kw, Vw = ring.gather_window(t)
+        toks = orc.effective_tokens(t, Tc, cfg.window_chunks, g_tok, shot * Tc, s_tok)
+        assert Kw.shape[0] == len(toks), (t, Kw.shape, len(toks))
+        if len(toks):
+            if full_check:
+                _, Kr, Vr = orc.gather_window(chunks, t, Tc, cfg.window_chunks, g_tok, shot * Tc,
+                                              s_tok)
+                kg, vg = bf16_np(Kw), bf16_np(Vw)
+                assert np.array_equal(kg, Kr), f"step {t}: K differs"
+                assert np.array_equal(vg, Vr), f"step {t}: V differs"
+            else:
+                idx = np.unique(np.concatenate([[0, len(toks) - 1],
+                                                np.random.default_rng(t).integers(0, len(toks), sample_tokens)]))
+                kg, vg = bf16_np(Kw[idx]), bf16_np(Vw[idx])
+                for j, i in enumerate(idx):
+                    tok = int(toks[i])
+                    c = tok // Tc
+                    kr = orc.kv_dequant_tokens(chunks[c], tok - c * Tc, 1, key=True)
+                    vr = orc.kv_dequant_tokens(chunks[c], tok - c * Tc, 1, key=False)
+                    assert np.array_equal(kg[j], kr[0]) and np.array_equal(vg[j], vr[0]), (t, tok)
+        Kg, Vg, K, V = chunk_inputs(seed, t, Tc, H, d)
+        ring.store_chunk(t, Kg, Vg)
+        chunks[t] = orc.kv_encode_chunk(K, V, search=cfg.search)
+        # drop chunks no step can reference any more (window and sinks)
+        for old in list(chunks):
+            if old not in (0, shot) and old < t + 1 - cfg.window_chunks:
+                del chunks[old]
+    torch.cuda.synchronize()
+    return ring, chunks
+
+
+def test_store_chunk_ring_bytes_bit_exact(nv, orc):
+    """Ring slot contents after one store equal the oracle's chunk encoding."""
+    cfg = nv.KVConfig(tokens_per_frame=40, frames_per_chunk=5, heads=3, head_dim=32,
+                      sink_frames_global=2, sink_frames_shot=1, window_chunks=2)
+    print("case: store chunk T=200 H=3 d=32", flush=True)
+    ring = nv.KVRing(cfg)
+    Kg, Vg, K, V = chunk_inputs(2002, 0, 200, 3, 32)
+    ring.store_chunk(0, Kg, Vg)
+    ref = orc.kv_encode_chunk(K, V)
+    torch.cuda.synchronize()
+    mem = ring.mem.cpu().numpy()[ring._base - ring.mem.data_ptr():]
+    T, HD = 200, 96
+    # slot 0 layout: K codes, K scales, V codes, V scales, mu, s_dec (each 256-aligned)
+    a = lambda n: (n + 255) // 256 * 256
+    o = 0
+    kc = mem[o:o + T * HD // 2]; o += a(T * HD // 2)
+    ks = mem[o:o + T * HD // 16]; o += a(T * HD // 16)
+    vc = mem[o:o + T * HD // 2]; o += a(T * HD // 2)
+    vs = mem[o:o + T * HD // 16]; o += a(T * HD // 16)
+    mu = mem[o:o + HD * 4].view(np.float32); o += a(HD * 4)
+    sd = mem[o:o + 8].view(np.float32)
+    assert np.array_equal(mu, ref["mu"])
+    assert sd[0] == ref["sdk"] and sd[1] == ref["sdv"]
+    assert np.array_equal(kc, ref["kc"].ravel())
+    assert np.array_equal(ks, ref["ks"].ravel())
+    assert np.array_equal(vc, ref["vc"].ravel())
+    assert np.array_equal(vs, ref["vs"].ravel())
+
+
+def test_ring_small_geometry_all_segments(nv, orc):
+    """Small ring over 14 steps: global sink in and out of the window, shot
+    sinks rebound at prompt switches, overlapping sinks, window wrap-around."""
+    print("case: ring Tc=48 W=2 14 steps", flush=True)
+    cfg = nv.KVConfig(tokens_per_frame=12, frames_per_chunk=4, heads=2, head_dim=32,
+                      sink_frames_global=2, sink_frames_shot=1, window_chunks=2)
+    run_ring(nv, orc, cfg, cuts={0, 3, 4, 9}, steps=14, seed=77)
+
+
+def test_ring_search6_and_window1(nv, orc):
+    cfg = nv.KVConfig(tokens_per_frame=16, frames_per_chunk=2, heads=1, head_dim=64,
+                      sink_frames_global=1, sink_frames_shot=2, window_chunks=1,
+                      search=nv.SEARCH_6)
+    run_ring(nv, orc, cfg, cuts={0, 2, 5}, steps=9, seed=78)
+
+
+def test_ring_64s_schedule_one_head(nv, orc):
+    """The 64 s schedule (40 chunks of 7040 tokens, cuts every 10 chunks, 3-frame
+    sinks, W = 4) with one 128-wide head, every gathered value checked."""
+    print("case: ring 64s schedule H=1", flush=True)
+    cfg = nv.KVConfig(heads=1, head_dim=128)
+    run_ring(nv, orc, cfg, cuts={0, 10, 20, 30}, steps=40, seed=1005)
+
+
+def test_ring_full_geometry_sampled(nv, orc):
+    """Full chunk geometry (7040 x 24 x 128) for 7 steps (global sink leaves the
+    window at step 5), sampled gathered tokens checked."""
+    print("case: ring full geometry 7 steps", flush=True)
+    cfg = nv.KVConfig()
+    run_ring(nv, orc, cfg, cuts={0}, steps=7, seed=1002, full_check=False, sample_tokens=48)
+
+
+def test_gather_capacity_error(nv):
+    cfg = nv.KVConfig(tokens_per_frame=8, frames_per_chunk=2, heads=1, head_dim=16,
+                      sink_frames_global=1, sink_frames_shot=1, window_chunks=2)
+    ring = nv.KVRing(cfg)
+    Kg = torch.zeros((16, 1, 16), dtype=torch.bfloat16, device="cuda")
+    ring.store_chunk(0, Kg, Kg)
+    small = torch.empty((4, 1, 16), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(nv.NVFP4Error):
+        ring.gather_window(1, small, small)
+    with pytest.raises(nv.NVFP4Error):
+        ring.store_chunk(5, Kg, Kg)
+    torch.cuda.synchronize()
