@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=4, help="rotated input/output buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one plain device copy of 256 MiB first (for scaling HBM counters)")
     return ap.parse_args()
 
 
@@ -160,7 +162,7 @@ def setup_kv_chunk(nv, args, dev):
     return step, {"K": kb, "V": vb}
 
 
-def cpu_baseline_kv(sample_tokens=880):
+def cpu_baseline_kv(sample_tokens=KV_T):
     """The oracle (single-threaded C) on one frame's worth of tokens of the
     chunk: K-smoothing + 4/6 quantization of K and V, then dequantization of
     both back to bf16.  Returned in GB/s of the same algorithmic bytes."""
@@ -180,7 +182,7 @@ def cpu_baseline_kv(sample_tokens=880):
     dt = time.perf_counter() - t0
     alg = 2 * kv_bytes_per_chunk(T=sample_tokens)
     return {"value": alg / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"one 880-token frame of the chunk ({sample_tokens}x{KV_H}x{KV_D} K and V, "
+            "sample": f"{sample_tokens} tokens of the chunk ({sample_tokens}x{KV_H}x{KV_D} K and V, "
                       f"store + dequantize), {dt:.1f} s single-threaded"}
 
 
@@ -316,6 +318,13 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        # a plain copy of known size: 256 MiB read + 256 MiB written
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     if args.workload != "kv_chunk":
         fn = {"gemm_attn": run_gemm_attn, "ffn": run_ffn, "ring64s": run_ring64s,

@@ -153,7 +153,7 @@ int nvfp4_gemm_w4a4(const nvfp4_tensor *a, const nvfp4_tensor *w, void *y, int32
  * head_dim], token-major, T_c = tokens_per_frame * frames_per_chunk.
  */
 typedef struct nvfp4_kv_config {
-    int32_t tokens_per_frame;   /* L_f  (880) */
+    int32_t tokens_per_frame;   /* L_f  (880); T_c <= 65536, T_c*H*d < 2^31 */
     int32_t frames_per_chunk;   /* F_c  (8)   */
     int32_t heads;              /* H    (24)  */
     int32_t head_dim;           /* d    (128), multiple of 16 */

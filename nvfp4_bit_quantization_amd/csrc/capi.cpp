@@ -100,9 +100,9 @@ int check_kv_config(const nvfp4_kv_config *c) {
         return fail(NVFP4_EINVAL, "kv config: bad search %d", c->search);
     const int64_t T = (int64_t)c->tokens_per_frame * c->frames_per_chunk;
     const int64_t hd = (int64_t)c->heads * c->head_dim;
-    if (T * hd >= ((int64_t)1 << 31))
-        return fail(NVFP4_ESHAPE, "kv config: a chunk of %lld elements is too large",
-                    (long long)(T * hd));
+    if (T * hd >= ((int64_t)1 << 31) || T > 65536)
+        return fail(NVFP4_ESHAPE, "kv config: a chunk of %lld tokens x %lld channels is too large",
+                    (long long)T, (long long)hd);
     return NVFP4_OK;
 }
 

@@ -99,6 +99,52 @@ __device__ __forceinline__ float half_block_error(const float (&x)[8], uint32_t 
 }
 
 // ---------------------------------------------------------------------------
+// one 1x16 block held by one lane: the Four-Over-Six encoder
+// ---------------------------------------------------------------------------
+
+// Per-scale-code table entry: (S, r) with S = RN(sigma * s_dec) and
+// r = RN(1 / S) (0 when S == 0), sigma the E4M3 value of the code.
+__device__ __forceinline__ f32x2 scale_entry(uint32_t code, float s_dec) {
+    const float S = e4m3_value(code) * s_dec;
+    return f32x2{S, (S == 0.0f) ? 0.0f : 1.0f / S};
+}
+
+// Encode x_0..x_15 for the tensor encode scale s_enc.  For each target c in
+// {6, 4}: scale code E4M3(RN(RN(amax / c) * s_enc)), codes E2M1(RN(x * r)),
+// error RN(E_lo + E_hi) with E_lo / E_hi the fma chains of RN(x - V*S)^2
+// over elements 0..7 / 8..15; target 4 is kept only if its error is lower.
+// Codes of elements 0..7 go to q_lo, 8..15 to q_hi (element 2j in the low
+// nibble of byte j).
+template <bool FOUR_OVER_SIX>
+__device__ __forceinline__ void encode_block16(const float (&x)[16], float s_enc,
+                                               const f32x2 *lut, uint32_t &q_lo, uint32_t &q_hi,
+                                               uint32_t &scale) {
+    const float(&xl)[8] = *reinterpret_cast<const float(*)[8]>(&x[0]);
+    const float(&xh)[8] = *reinterpret_cast<const float(*)[8]>(&x[8]);
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(x[i]));
+    const uint32_t sc6 = e4m3_encode((am / 6.0f) * s_enc);
+    const f32x2 sr6 = lut[sc6];
+    const uint32_t a6 = e2m1_pack8(xl, sr6.y), b6 = e2m1_pack8(xh, sr6.y);
+    if (!FOUR_OVER_SIX) {
+        q_lo = a6;
+        q_hi = b6;
+        scale = sc6;
+        return;
+    }
+    const float e6 = half_block_error(xl, a6, sr6.x) + half_block_error(xh, b6, sr6.x);
+    const uint32_t sc4 = e4m3_encode((am * 0.25f) * s_enc);
+    const f32x2 sr4 = lut[sc4];
+    const uint32_t a4 = e2m1_pack8(xl, sr4.y), b4 = e2m1_pack8(xh, sr4.y);
+    const float e4 = half_block_error(xl, a4, sr4.x) + half_block_error(xh, b4, sr4.x);
+    const bool pick4 = e4 < e6;
+    q_lo = pick4 ? a4 : a6;
+    q_hi = pick4 ? b4 : b6;
+    scale = pick4 ? sc4 : sc6;
+}
+
+// ---------------------------------------------------------------------------
 // lane exchange
 // ---------------------------------------------------------------------------
 
@@ -128,6 +174,45 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     __builtin_memcpy(&ub, &hb, 2);
     return (uint32_t)ua | ((uint32_t)ub << 16);
 }
+
+// Raw 16-element block loads (16 bf16 = 2 x 16 B, 16 float = 4 x 16 B).
+struct Raw16Bf16 {
+    u32x4 a, b;
+};
+struct Raw16F32 {
+    f32x4 a, b, c, d;
+};
+__device__ __forceinline__ void load_raw16(const uint16_t *p, Raw16Bf16 &r) {
+    r.a = *(const u32x4 *)p;
+    r.b = *(const u32x4 *)(p + 8);
+}
+__device__ __forceinline__ void load_raw16(const float *p, Raw16F32 &r) {
+    r.a = *(const f32x4 *)p;
+    r.b = *(const f32x4 *)(p + 4);
+    r.c = *(const f32x4 *)(p + 8);
+    r.d = *(const f32x4 *)(p + 12);
+}
+__device__ __forceinline__ void unpack16(const Raw16Bf16 &r, float (&x)[16]) {
+    const uint32_t w[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        x[2 * i] = bf16lo(w[i]);
+        x[2 * i + 1] = bf16hi(w[i]);
+    }
+}
+__device__ __forceinline__ void unpack16(const Raw16F32 &r, float (&x)[16]) {
+    const f32x4 v[4] = {r.a, r.b, r.c, r.d};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[4 * i] = v[i].x;
+        x[4 * i + 1] = v[i].y;
+        x[4 * i + 2] = v[i].z;
+        x[4 * i + 3] = v[i].w;
+    }
+}
+template <typename T> struct Raw16Of;
+template <> struct Raw16Of<uint16_t> { typedef Raw16Bf16 type; };
+template <> struct Raw16Of<float> { typedef Raw16F32 type; };
 
 // Load 8 consecutive elements as float.
 __device__ __forceinline__ void load8(const float *p, float (&x)[8]) {

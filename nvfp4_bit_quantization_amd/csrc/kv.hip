@@ -28,219 +28,316 @@
 
 namespace nvfp4 {
 
-constexpr int kTile = 64;          // tokens per statistics tile
-constexpr int kStatsLanes = 64;    // lanes per stats workgroup (8 channels each)
+// Key-mean summation order (fixed, so the result is reproducible): tokens in
+// tiles of kSeq = 16, each tile summed in token order in double; the tile
+// sums, padded with zeros to a power-of-two count, added pairwise level by
+// level.  kv_stats computes the tile sums and the first two tree levels (one
+// workgroup = 4 waves = 4 consecutive tiles); kv_finalize finishes the tree.
+constexpr int kSeq = 16;            // tokens summed sequentially by one lane
+constexpr int kStatsTokens = 64;    // tokens per stats workgroup (4 waves x 16)
+constexpr int kGroupCh = 512;       // channels per stats workgroup (64 lanes x 8)
+constexpr int kFinCh = 64;          // channels per finalize workgroup
 
 struct KvWs {
-    double *P;       // [ntiles, HD]
-    float *kmax;     // [ntiles, HD]
-    float *kmin;     // [ntiles, HD]
-    float *vpart;    // [ntiles * gy]
-    float *senc;     // [2]
+    double *P;      // [nt64, HD]  level-2 tree nodes (64-token sums)
+    float *kmax;    // [nt64, HD]
+    float *kmin;    // [nt64, HD]
+    float *vpart;   // [nt64 * gy] value |max| per stats workgroup
+    float *kpart;   // [nfin]      key amax per finalize workgroup
+};
+
+struct KvDims {
+    int64_t nt64;   // stats workgroups along tokens
+    int64_t gy;     // stats workgroups along channels
+    int64_t n2;     // level-2 nodes in the padded tree (power of two)
+    int64_t nfin;   // finalize workgroups
 };
 
 static inline int64_t align256(int64_t b) { return (b + 255) & ~(int64_t)255; }
 
+static KvDims kv_dims(int64_t T, int64_t HD) {
+    KvDims d;
+    d.nt64 = (T + kStatsTokens - 1) / kStatsTokens;
+    d.gy = (HD + kGroupCh - 1) / kGroupCh;
+    const int64_t nt16 = (T + kSeq - 1) / kSeq;
+    int64_t npad = 1;
+    while (npad < nt16) npad *= 2;
+    d.n2 = npad >= 4 ? npad / 4 : 1;
+    d.nfin = (HD + kFinCh - 1) / kFinCh;
+    return d;
+}
+
 static KvWs carve_ws(void *ws, int64_t T, int64_t HD) {
-    const int64_t ntiles = (T + kTile - 1) / kTile;
-    const int64_t gy = (HD / 8 + kStatsLanes - 1) / kStatsLanes;
+    const KvDims d = kv_dims(T, HD);
     uint8_t *p = (uint8_t *)ws;
     KvWs w;
     w.P = (double *)p;
-    p += align256(ntiles * HD * 8);
+    p += align256(d.nt64 * HD * 8);
     w.kmax = (float *)p;
-    p += align256(ntiles * HD * 4);
+    p += align256(d.nt64 * HD * 4);
     w.kmin = (float *)p;
-    p += align256(ntiles * HD * 4);
+    p += align256(d.nt64 * HD * 4);
     w.vpart = (float *)p;
-    p += align256(ntiles * gy * 4);
-    w.senc = (float *)p;
+    p += align256(d.nt64 * d.gy * 4);
+    w.kpart = (float *)p;
     return w;
 }
 
 size_t kv_store_ws_bytes(int64_t T, int64_t HD) {
-    const int64_t ntiles = (T + kTile - 1) / kTile;
-    const int64_t gy = (HD / 8 + kStatsLanes - 1) / kStatsLanes;
-    return (size_t)(align256(ntiles * HD * 8) + 2 * align256(ntiles * HD * 4) +
-                    align256(ntiles * gy * 4) + 256);
+    const KvDims d = kv_dims(T, HD);
+    return (size_t)(align256(d.nt64 * HD * 8) + 2 * align256(d.nt64 * HD * 4) +
+                    align256(d.nt64 * d.gy * 4) + align256(d.nfin * 4));
 }
 
-__global__ __launch_bounds__(64) void kv_stats_kernel(const uint16_t *__restrict__ K,
-                                                      const uint16_t *__restrict__ V, int64_t T,
-                                                      int64_t HD, KvWs w) {
+// Workgroup (tile p of 64 tokens, channel group g of 512, blockIdx.z = 0):
+// wave w sums tokens 64p + 16w .. +15 of its lane's 8 channels sequentially;
+// the four wave sums are combined as ((s0 + s1) + (s2 + s3)); key max/min
+// per channel.  blockIdx.z = 1 workgroups take the value |max| of the same
+// tile.  Loads are unconditional (token index clamped) so that all 16 of a
+// lane's loads are in flight together; out-of-range tokens contribute +0 to
+// the sums (no partial sum is -0, so adding +0 changes nothing) and nothing
+// to the extrema.
+__global__ __launch_bounds__(256) void kv_stats_kernel(const uint16_t *__restrict__ K,
+                                                       const uint16_t *__restrict__ V, int64_t T,
+                                                       int64_t HD, KvWs w) {
+    __shared__ double sp[4][kGroupCh];
+    __shared__ float smx[4][kGroupCh];
+    __shared__ float smn[4][kGroupCh];
+    __shared__ float svm[4];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t p = blockIdx.x;
-    const int64_t ch0 = ((int64_t)blockIdx.y * kStatsLanes + threadIdx.x) * 8;
-    const int64_t t0 = p * kTile;
-    const int64_t t1 = (t0 + kTile < T) ? t0 + kTile : T;
-    float vmx = 0.0f;
-    if (ch0 < HD) {
-        double s[8];
-        float mx[8], mn[8];
+    const int chl = lane * 8;
+    const int64_t chq = (int64_t)blockIdx.y * kGroupCh + chl;
+    const bool ch_ok = chq < HD;
+    const int64_t ch0 = ch_ok ? chq : 0;
+    const int64_t t0 = p * kStatsTokens + wave * kSeq;
+    u32x4 r[kSeq];
+    const uint16_t *src = blockIdx.z ? V : K;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            s[i] = 0.0;
-            mx[i] = -__builtin_huge_valf();
-            mn[i] = __builtin_huge_valf();
+    for (int j = 0; j < kSeq; ++j) {
+        const int64_t t = (t0 + j < T) ? t0 + j : T - 1;
+        r[j] = *(const u32x4 *)(src + t * HD + ch0);
+    }
+    if (blockIdx.z) {
+        float vmx = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kSeq; ++j) {
+            const bool ok = ch_ok && (t0 + j < T);
+            const uint32_t vw[4] = {r[j].x, r[j].y, r[j].z, r[j].w};
+            float m = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                m = fmaxf(m, fmaxf(fabsf(bf16lo(vw[q])), fabsf(bf16hi(vw[q]))));
+            vmx = ok ? fmaxf(vmx, m) : vmx;
         }
-        for (int64_t t = t0; t < t1; ++t) {
-            float k[8], v[8];
-            load8(K + t * HD + ch0, k);
-            load8(V + t * HD + ch0, v);
+        vmx = wave_max(vmx);
+        if (lane == 0) svm[wave] = vmx;
+        __syncthreads();
+        if (threadIdx.x == 0)
+            w.vpart[p * gridDim.y + blockIdx.y] =
+                fmaxf(fmaxf(svm[0], svm[1]), fmaxf(svm[2], svm[3]));
+        return;
+    }
+    double s[8];
+    float mx[8], mn[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                s[i] += (double)k[i];
-                mx[i] = fmaxf(mx[i], k[i]);
-                mn[i] = fminf(mn[i], k[i]);
-                vmx = fmaxf(vmx, fabsf(v[i]));
-            }
-        }
+    for (int i = 0; i < 8; ++i) {
+        s[i] = 0.0;
+        mx[i] = -__builtin_huge_valf();
+        mn[i] = __builtin_huge_valf();
+    }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            w.P[p * HD + ch0 + i] = s[i];
-            w.kmax[p * HD + ch0 + i] = mx[i];
-            w.kmin[p * HD + ch0 + i] = mn[i];
+    for (int j = 0; j < kSeq; ++j) {
+        const bool ok = t0 + j < T;
+        const uint32_t kw[4] = {r[j].x, r[j].y, r[j].z, r[j].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float a = bf16lo(kw[q]), b = bf16hi(kw[q]);
+            s[2 * q] += ok ? (double)a : 0.0;
+            s[2 * q + 1] += ok ? (double)b : 0.0;
+            mx[2 * q] = ok ? fmaxf(mx[2 * q], a) : mx[2 * q];
+            mx[2 * q + 1] = ok ? fmaxf(mx[2 * q + 1], b) : mx[2 * q + 1];
+            mn[2 * q] = ok ? fminf(mn[2 * q], a) : mn[2 * q];
+            mn[2 * q + 1] = ok ? fminf(mn[2 * q + 1], b) : mn[2 * q + 1];
         }
     }
-    vmx = wave_max(vmx);
-    if (threadIdx.x == 0) w.vpart[p * gridDim.y + blockIdx.y] = vmx;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        sp[wave][chl + i] = s[i];
+        smx[wave][chl + i] = mx[i];
+        smn[wave][chl + i] = mn[i];
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < kGroupCh; c += blockDim.x) {
+        const int64_t ch = (int64_t)blockIdx.y * kGroupCh + c;
+        if (ch < HD) {
+            const double P = (sp[0][c] + sp[1][c]) + (sp[2][c] + sp[3][c]);
+            w.P[p * HD + ch] = P;
+            w.kmax[p * HD + ch] = fmaxf(fmaxf(smx[0][c], smx[1][c]), fmaxf(smx[2][c], smx[3][c]));
+            w.kmin[p * HD + ch] = fminf(fminf(smn[0][c], smn[1][c]), fminf(smn[2][c], smn[3][c]));
+        }
+    }
 }
 
-__global__ __launch_bounds__(1024) void kv_finalize_kernel(KvWs w, int64_t ntiles, int64_t nvpart,
-                                                           int64_t T, int64_t HD, float *mu_slot,
-                                                           float *mu_g, float *mu_s,
-                                                           float *sd_slot, float *sd_g,
-                                                           float *sd_s) {
-    __shared__ float red[2][16];
-    float ak = 0.0f, av = 0.0f;
-    for (int64_t ch = threadIdx.x; ch < HD; ch += blockDim.x) {
-        double S = 0.0;
-        float kx = -__builtin_huge_valf(), kn = __builtin_huge_valf();
-        for (int64_t p = 0; p < ntiles; ++p) {
-            S += w.P[p * HD + ch];
-            kx = fmaxf(kx, w.kmax[p * HD + ch]);
-            kn = fminf(kn, w.kmin[p * HD + ch]);
+// Tree sum of 32 doubles, adjacent pairs level by level.
+__device__ __forceinline__ double tree32(double (&v)[32]) {
+#pragma unroll
+    for (int w = 16; w >= 1; w >>= 1)
+#pragma unroll
+        for (int i = 0; i < w; ++i) v[i] = v[2 * i] + v[2 * i + 1];
+    return v[0];
+}
+
+// Workgroup of 256 threads = 4 waves over 64 channels (lane = channel).  The
+// level-2 nodes of a channel form blocks of 32 (nodes past the last 64-token
+// tile are zero); wave q sums blocks q, q+4, ... with a fixed 32-leaf tree
+// into LDS, then wave 0 sums the block sums with the same tree (zero padded;
+// adding an exact zero changes nothing, and no partial sum is -0).  This is
+// the level-by-level pairwise tree over the 16-token tile sums.
+// mu = (float)(S / T); the workgroup's key amax
+// max_c max(RN(max K - mu), RN(mu - min K)) goes to kpart.
+__global__ __launch_bounds__(256) void kv_finalize_kernel(KvWs w, int64_t nt64, int64_t n2,
+                                                          int64_t T, int64_t HD, float *mu_slot,
+                                                          float *mu_g, float *mu_s) {
+    __shared__ double bs[32][kFinCh];
+    __shared__ float rx[4][kFinCh];
+    __shared__ float rn[4][kFinCh];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t ch = (int64_t)blockIdx.x * kFinCh + lane;
+    const int nb = n2 >= 32 ? (int)(n2 / 32) : 1;  // blocks of 32 nodes (<= 32)
+    float kx = -__builtin_huge_valf(), kn = __builtin_huge_valf();
+    const int64_t chc = ch < HD ? ch : HD - 1;
+    for (int b = wave; b < nb; b += 4) {
+        double v[32];
+        float xv[32], nv[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const int64_t node = (int64_t)b * 32 + i;
+            const int64_t nc = node < nt64 ? node : nt64 - 1;
+            v[i] = w.P[nc * HD + chc];
+            xv[i] = w.kmax[nc * HD + chc];
+            nv[i] = w.kmin[nc * HD + chc];
         }
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const bool ok = (int64_t)b * 32 + i < nt64;
+            v[i] = ok ? v[i] : 0.0;
+            kx = ok ? fmaxf(kx, xv[i]) : kx;
+            kn = ok ? fminf(kn, nv[i]) : kn;
+        }
+        bs[b][lane] = tree32(v);
+    }
+    rx[wave][lane] = kx;
+    rn[wave][lane] = kn;
+    __syncthreads();
+    if (wave != 0) return;
+    float amax = 0.0f;
+    if (ch < HD) {
+        double v[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) v[i] = (i < nb) ? bs[i][lane] : 0.0;
+        const double S = tree32(v);
         const float mu = (float)(S / (double)T);
         mu_slot[ch] = mu;
         if (mu_g) mu_g[ch] = mu;
         if (mu_s) mu_s[ch] = mu;
-        ak = fmaxf(ak, fmaxf(kx - mu, mu - kn));
+        const float x = fmaxf(fmaxf(rx[0][lane], rx[1][lane]), fmaxf(rx[2][lane], rx[3][lane]));
+        const float n = fminf(fminf(rn[0][lane], rn[1][lane]), fminf(rn[2][lane], rn[3][lane]));
+        amax = fmaxf(x - mu, mu - n);
     }
-    for (int64_t i = threadIdx.x; i < nvpart; i += blockDim.x) av = fmaxf(av, w.vpart[i]);
+    amax = wave_max(amax);
+    if (lane == 0) w.kpart[blockIdx.x] = amax;
+}
+
+// One lane per 1x16 block along the (head, dim) axis; blockIdx.y = 0: keys
+// (K_s = RN(K - mu)), 1: values.  The prologue reduces the key / value amax
+// partials, derives both tensor scales (workgroup (0,0) stores the decode
+// scales into the slot and the sink copies) and builds the (S, r) table of
+// the workgroup's tensor.  Blocks below the sink length are also written to
+// the sink copies.
+template <bool FOUR_OVER_SIX>
+__global__ __launch_bounds__(256) void kv_encode_kernel(
+    const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, int64_t nblk, int64_t HD,
+    const float *__restrict__ kpart, int nk, const float *__restrict__ vpart, int nv,
+    KvRegion slot, KvRegion gsink, KvRegion ssink, int64_t g_blk, int64_t s_blk) {
+    __shared__ f32x2 lut[128];
+    __shared__ float red[2][4];
+    __shared__ float sh[4];
+    const int which = blockIdx.y;  // 0: keys, 1: values
+    float ak = 0.0f, av = 0.0f;
+    for (int i = threadIdx.x; i < nk; i += blockDim.x) ak = fmaxf(ak, kpart[i]);
+    for (int i = threadIdx.x; i < nv; i += blockDim.x) av = fmaxf(av, vpart[i]);
     ak = wave_max(ak);
     av = wave_max(av);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (lane == 0) {
-        red[0][wave] = ak;
-        red[1][wave] = av;
+    if ((threadIdx.x & 63) == 0) {
+        red[0][threadIdx.x >> 6] = ak;
+        red[1][threadIdx.x >> 6] = av;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        float a0 = 0.0f, a1 = 0.0f;
-        for (int i = 0; i < (int)(blockDim.x >> 6); ++i) {
-            a0 = fmaxf(a0, red[0][i]);
-            a1 = fmaxf(a1, red[1][i]);
-        }
+        const float a0 = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+        const float a1 = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
         float e0, d0, e1, d1;
         tensor_scales(a0, e0, d0);
         tensor_scales(a1, e1, d1);
-        w.senc[0] = e0;
-        w.senc[1] = e1;
-        sd_slot[0] = d0;
-        sd_slot[1] = d1;
-        if (sd_g) {
-            sd_g[0] = d0;
-            sd_g[1] = d1;
+        sh[0] = e0;
+        sh[1] = d0;
+        sh[2] = e1;
+        sh[3] = d1;
+        if (blockIdx.x == 0 && blockIdx.y == 0) {
+            slot.sd[0] = d0;
+            slot.sd[1] = d1;
+            if (g_blk > 0) {
+                gsink.sd[0] = d0;
+                gsink.sd[1] = d1;
+            }
+            if (s_blk > 0) {
+                ssink.sd[0] = d0;
+                ssink.sd[1] = d1;
+            }
         }
-        if (sd_s) {
-            sd_s[0] = d0;
-            sd_s[1] = d1;
-        }
-    }
-}
-
-// Encoder core shared in spirit with quantize.hip's 1-D encoder: lane = 8
-// elements, lane pair = one 1x16 block along the (head, dim) axis.
-template <bool FOUR_OVER_SIX>
-__device__ __forceinline__ void kv_encode_half(const float (&x)[8], float s_enc, const f32x2 *lut,
-                                               uint32_t &codes, uint32_t &scale) {
-    float am = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(x[i]));
-    am = fmaxf(am, swap_pair(am));
-    float id6 = (am / 6.0f) * s_enc;
-    uint32_t sc6 = e4m3_encode(id6);
-    f32x2 sr6 = lut[sc6];
-    uint32_t q6 = e2m1_pack8(x, sr6.y);
-    if (!FOUR_OVER_SIX) {
-        codes = q6;
-        scale = sc6;
-        return;
-    }
-    float e6 = half_block_error(x, q6, sr6.x);
-    float id4 = (am * 0.25f) * s_enc;
-    uint32_t sc4 = e4m3_encode(id4);
-    f32x2 sr4 = lut[sc4];
-    uint32_t q4 = e2m1_pack8(x, sr4.y);
-    float e4 = half_block_error(x, q4, sr4.x);
-    e6 = e6 + swap_pair(e6);
-    e4 = e4 + swap_pair(e4);
-    const bool pick4 = e4 < e6;
-    codes = pick4 ? q4 : q6;
-    scale = pick4 ? sc4 : sc6;
-}
-
-template <bool FOUR_OVER_SIX>
-__global__ __launch_bounds__(256) void kv_encode_kernel(const uint16_t *__restrict__ K,
-                                                        const uint16_t *__restrict__ V,
-                                                        int64_t n8, int64_t HD,
-                                                        const float *__restrict__ senc,
-                                                        KvRegion slot, KvRegion gsink,
-                                                        KvRegion ssink, int64_t g_n8,
-                                                        int64_t s_n8) {
-    __shared__ f32x2 lut[128];
-    const int which = blockIdx.y;  // 0: keys, 1: values
-    const float s_dec = slot.sd[which];
-    const float s_enc = senc[which];
-    for (int c = threadIdx.x; c < 128; c += blockDim.x) {
-        float S = e4m3_value((uint32_t)c) * s_dec;
-        lut[c] = f32x2{S, (S == 0.0f) ? 0.0f : 1.0f / S};
     }
     __syncthreads();
+    const float s_enc = sh[2 * which];
+    const float s_dec = sh[2 * which + 1];
+    for (int c = threadIdx.x; c < 128; c += blockDim.x) lut[c] = scale_entry((uint32_t)c, s_dec);
+    __syncthreads();
     const uint16_t *x = which ? V : K;
-    uint32_t *codes = (uint32_t *)(which ? slot.vc : slot.kc);
+    uint2 *codes = (uint2 *)(which ? slot.vc : slot.kc);
     uint8_t *scales = which ? slot.vs : slot.ks;
-    uint32_t *gcodes = (uint32_t *)(which ? gsink.vc : gsink.kc);
+    uint2 *gcodes = (uint2 *)(which ? gsink.vc : gsink.kc);
     uint8_t *gscales = which ? gsink.vs : gsink.ks;
-    uint32_t *scodes = (uint32_t *)(which ? ssink.vc : ssink.kc);
+    uint2 *scodes = (uint2 *)(which ? ssink.vc : ssink.kc);
     uint8_t *sscales = which ? ssink.vs : ssink.ks;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    // channel of the unit's first element, advanced incrementally (no division
-    // in the loop): ch0 = (8u) mod HD
-    int64_t ch0 = (u * 8) % HD;
-    const int64_t step = (stride * 8) % HD;
-    for (; u < n8; u += stride) {
-        float v[8];
-        load8(x + u * 8, v);
+    int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    // channel of the block's first element, advanced without division: (16 b) mod HD
+    int64_t ch0 = (b * 16) % HD;
+    const int64_t step = (stride * 16) % HD;
+    for (; b < nblk; b += stride) {
+        Raw16Bf16 r;
+        load_raw16(x + b * 16, r);
+        float v[16];
+        unpack16(r, v);
         if (which == 0) {
-            float m[8];
-            load8(slot.mu + ch0, m);
+            Raw16F32 m;
+            load_raw16(slot.mu + ch0, m);
+            float mu[16];
+            unpack16(m, mu);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = v[i] - m[i];
+            for (int i = 0; i < 16; ++i) v[i] = v[i] - mu[i];
         }
-        uint32_t q, sc;
-        kv_encode_half<FOUR_OVER_SIX>(v, s_enc, lut, q, sc);
-        codes[u] = q;
-        const bool lead = (u & 1) == 0;
-        if (lead) scales[u >> 1] = (uint8_t)sc;
-        if (u < g_n8) {
-            gcodes[u] = q;
-            if (lead) gscales[u >> 1] = (uint8_t)sc;
+        uint32_t lo, hi, sc;
+        encode_block16<FOUR_OVER_SIX>(v, s_enc, lut, lo, hi, sc);
+        codes[b] = make_uint2(lo, hi);
+        scales[b] = (uint8_t)sc;
+        if (b < g_blk) {
+            gcodes[b] = make_uint2(lo, hi);
+            gscales[b] = (uint8_t)sc;
         }
-        if (u < s_n8) {
-            scodes[u] = q;
-            if (lead) sscales[u >> 1] = (uint8_t)sc;
+        if (b < s_blk) {
+            scodes[b] = make_uint2(lo, hi);
+            sscales[b] = (uint8_t)sc;
         }
         ch0 += step;
         if (ch0 >= HD) ch0 -= HD;
@@ -248,33 +345,32 @@ __global__ __launch_bounds__(256) void kv_encode_kernel(const uint16_t *__restri
 }
 
 hipError_t launch_kv_store(const KvStoreArgs &a, hipStream_t s) {
-    const int64_t ntiles = (a.T + kTile - 1) / kTile;
-    const int64_t gy = (a.HD / 8 + kStatsLanes - 1) / kStatsLanes;
+    const KvDims d = kv_dims(a.T, a.HD);
     KvWs w = carve_ws(a.ws, a.T, a.HD);
-    NVFP4_LAUNCH("kv_stats", kv_stats_kernel, dim3((unsigned)ntiles, (unsigned)gy),
-                 dim3(kStatsLanes), 0, s, a.K, a.V, a.T, a.HD, w);
+    NVFP4_LAUNCH("kv_stats", kv_stats_kernel, dim3((unsigned)d.nt64, (unsigned)d.gy, 2),
+                 dim3(256), 0, s, a.K, a.V, a.T, a.HD, w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    NVFP4_LAUNCH("kv_finalize", kv_finalize_kernel, dim3(1), dim3(1024), 0, s, w, ntiles, ntiles * gy,
-                       a.T, a.HD, a.slot.mu, a.g_tokens > 0 ? a.gsink.mu : (float *)nullptr,
-                       a.s_tokens > 0 ? a.ssink.mu : (float *)nullptr, a.slot.sd,
-                       a.g_tokens > 0 ? a.gsink.sd : (float *)nullptr,
-                       a.s_tokens > 0 ? a.ssink.sd : (float *)nullptr);
+    NVFP4_LAUNCH("kv_finalize", kv_finalize_kernel, dim3((unsigned)d.nfin), dim3(256), 0, s, w,
+                 d.nt64, d.n2, a.T, a.HD, a.slot.mu,
+                 a.g_tokens > 0 ? a.gsink.mu : (float *)nullptr,
+                 a.s_tokens > 0 ? a.ssink.mu : (float *)nullptr);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t n8 = a.T * a.HD / 8;
-    int64_t g = (n8 + 1023) / 1024;
-    if (g > 4096) g = 4096;
+    const int64_t nblk = a.T * a.HD / 16;
+    int64_t g = (nblk + 255) / 256;
+    if (g > 512) g = 512;
     if (g < 1) g = 1;
-    const int64_t g_n8 = a.g_tokens * a.HD / 8, s_n8 = a.s_tokens * a.HD / 8;
+    const int64_t g_blk = a.g_tokens * a.HD / 16, s_blk = a.s_tokens * a.HD / 16;
+    const int nk = (int)d.nfin, nv = (int)(d.nt64 * d.gy);
     if (a.search == 1)
-        NVFP4_LAUNCH("kv_encode", kv_encode_kernel<true>, dim3((unsigned)g, 2), dim3(256), 0, s, a.K,
-                           a.V, n8, a.HD, (const float *)w.senc, a.slot, a.gsink, a.ssink, g_n8,
-                           s_n8);
+        NVFP4_LAUNCH("kv_encode", kv_encode_kernel<true>, dim3((unsigned)g, 2), dim3(256), 0, s,
+                     a.K, a.V, nblk, a.HD, (const float *)w.kpart, nk, (const float *)w.vpart, nv,
+                     a.slot, a.gsink, a.ssink, g_blk, s_blk);
     else
-        NVFP4_LAUNCH("kv_encode", kv_encode_kernel<false>, dim3((unsigned)g, 2), dim3(256), 0, s, a.K,
-                           a.V, n8, a.HD, (const float *)w.senc, a.slot, a.gsink, a.ssink, g_n8,
-                           s_n8);
+        NVFP4_LAUNCH("kv_encode", kv_encode_kernel<false>, dim3((unsigned)g, 2), dim3(256), 0, s,
+                     a.K, a.V, nblk, a.HD, (const float *)w.kpart, nk, (const float *)w.vpart, nv,
+                     a.slot, a.gsink, a.ssink, g_blk, s_blk);
     return hipGetLastError();
 }
 
@@ -285,59 +381,93 @@ hipError_t launch_kv_store(const KvStoreArgs &a, hipStream_t s) {
 // Output order: [global-sink tokens outside the window][shot-sink tokens
 // outside the window][window chunks c_lo .. c_lo + nwin - 1]; sinks lie below
 // the window in token order, so this is ascending token order.
-__global__ __launch_bounds__(1024) void kv_gather_kernel(GatherArgs a) {
-    const int64_t U = a.HD >> 3;   // 8-element units per token
-    const int64_t SB = a.HD >> 4;  // scale bytes per token
-    for (int64_t tok = blockIdx.x; tok < a.n_tokens; tok += gridDim.x) {
-        KvRegion r;
-        int64_t st;
-        if (tok < a.n_g) {
-            r = a.gsink;
-            st = tok;
-        } else if (tok < a.n_g + a.n_s) {
-            r = a.ssink;
-            st = tok - a.n_g;
-        } else {
-            const int64_t w = tok - a.n_g - a.n_s;
-            const int64_t q = w / a.Tc;
-            const int64_t off = ((a.c_lo + q) % a.W) * a.slot_bytes;
-            r.kc = a.slot0.kc + off;
-            r.ks = a.slot0.ks + off;
-            r.vc = a.slot0.vc + off;
-            r.vs = a.slot0.vs + off;
-            r.mu = (float *)((uint8_t *)a.slot0.mu + off);
-            r.sd = (float *)((uint8_t *)a.slot0.sd + off);
-            st = w - q * a.Tc;
-        }
-        const float sdk = r.sd[0], sdv = r.sd[1];
-        const uint32_t *kc = (const uint32_t *)r.kc + st * U;
-        const uint32_t *vc = (const uint32_t *)r.vc + st * U;
-        const uint8_t *ks = r.ks + st * SB;
-        const uint8_t *vs = r.vs + st * SB;
-        uint16_t *ko = a.Kout + tok * a.HD;
-        uint16_t *vo = a.Vout + tok * a.HD;
-        for (int64_t j = threadIdx.x; j < U; j += blockDim.x) {
-            const uint32_t qk = kc[j], qv = vc[j];
-            const float Sk = e4m3_value(ks[j >> 1]) * sdk;
-            const float Sv = e4m3_value(vs[j >> 1]) * sdv;
-            float yk[8], yv[8], m[8];
-            dequant8(qk, Sk, yk);
-            dequant8(qv, Sv, yv);
-            load8(r.mu + j * 8, m);
+__device__ __forceinline__ void gather_region(const GatherArgs &a, int64_t tok, KvRegion &r,
+                                              int64_t &st) {
+    if (tok < a.n_g) {
+        r = a.gsink;
+        st = tok;
+    } else if (tok < a.n_g + a.n_s) {
+        r = a.ssink;
+        st = tok - a.n_g;
+    } else {
+        const int64_t w = tok - a.n_g - a.n_s;
+        const int64_t q = w / a.Tc;
+        const int64_t off = ((a.c_lo + q) % a.W) * a.slot_bytes;
+        r.kc = a.slot0.kc + off;
+        r.ks = a.slot0.ks + off;
+        r.vc = a.slot0.vc + off;
+        r.vs = a.slot0.vs + off;
+        r.mu = (float *)((uint8_t *)a.slot0.mu + off);
+        r.sd = (float *)((uint8_t *)a.slot0.sd + off);
+        st = w - q * a.Tc;
+    }
+}
+
+// Each workgroup-iteration covers kGatherTok consecutive output tokens; lane
+// j expands block j (16 elements) of K and V of each of them, with the loads
+// of all the tokens issued before any of them is expanded.
+constexpr int kGatherTok = 4;
+
+__global__ __launch_bounds__(256) void kv_gather_kernel(GatherArgs a) {
+    const int64_t NB = a.HD >> 4;  // blocks per token
+    for (int64_t tok0 = (int64_t)blockIdx.x * kGatherTok; tok0 < a.n_tokens;
+         tok0 += (int64_t)gridDim.x * kGatherTok) {
+        for (int64_t j = threadIdx.x; j < NB; j += blockDim.x) {
+            uint2 qk[kGatherTok], qv[kGatherTok];
+            uint32_t sk[kGatherTok], sv[kGatherTok];
+            const float *mup[kGatherTok];
+            float sdk[kGatherTok], sdv[kGatherTok];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) yk[i] = yk[i] + m[i];
-            store8(ko + j * 8, yk);
-            store8(vo + j * 8, yv);
+            for (int k = 0; k < kGatherTok; ++k) {
+                const int64_t tok = tok0 + k < a.n_tokens ? tok0 + k : a.n_tokens - 1;
+                KvRegion r;
+                int64_t st;
+                gather_region(a, tok, r, st);
+                qk[k] = ((const uint2 *)r.kc)[st * NB + j];
+                qv[k] = ((const uint2 *)r.vc)[st * NB + j];
+                sk[k] = r.ks[st * NB + j];
+                sv[k] = r.vs[st * NB + j];
+                sdk[k] = r.sd[0];
+                sdv[k] = r.sd[1];
+                mup[k] = r.mu + j * 16;
+            }
+#pragma unroll
+            for (int k = 0; k < kGatherTok; ++k) {
+                const int64_t tok = tok0 + k;
+                if (tok >= a.n_tokens) break;
+                Raw16F32 m;
+                load_raw16(mup[k], m);
+                float mu[16];
+                unpack16(m, mu);
+                const float Sk = e4m3_value(sk[k]) * sdk[k];
+                const float Sv = e4m3_value(sv[k]) * sdv[k];
+                uint16_t *ko = a.Kout + tok * a.HD + j * 16;
+                uint16_t *vo = a.Vout + tok * a.HD + j * 16;
+                float y[8];
+                dequant8(qk[k].x, Sk, y);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) y[i] = y[i] + mu[i];
+                store8(ko, y);
+                dequant8(qk[k].y, Sk, y);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) y[i] = y[i] + mu[8 + i];
+                store8(ko + 8, y);
+                dequant8(qv[k].x, Sv, y);
+                store8(vo, y);
+                dequant8(qv[k].y, Sv, y);
+                store8(vo + 8, y);
+            }
         }
     }
 }
 
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s) {
     if (a.n_tokens == 0) return hipSuccess;
-    const int64_t U = a.HD >> 3;
-    int64_t bs = ((U + 63) / 64) * 64;
-    if (bs > 1024) bs = 1024;
-    int64_t g = a.n_tokens < 4096 ? a.n_tokens : 4096;
+    const int64_t NB = a.HD >> 4;
+    int64_t bs = ((NB + 63) / 64) * 64;
+    if (bs > 256) bs = 256;
+    int64_t g = (a.n_tokens + kGatherTok - 1) / kGatherTok;
+    if (g > 2048) g = 2048;
     NVFP4_LAUNCH("kv_gather", kv_gather_kernel, dim3((unsigned)g), dim3((unsigned)bs), 0, s, a);
     return hipGetLastError();
 }

@@ -24,7 +24,7 @@ void prof_end(int idx, hipStream_t s);
 
 constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
-constexpr int kMaxPartials = 2048;  // amax partials per quantize call
+constexpr int kMaxPartials = 1024;  // amax partials per quantize call
 
 // ---- quantize.hip
 int amax_partials_for(int64_t n);

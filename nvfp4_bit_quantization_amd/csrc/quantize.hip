@@ -31,11 +31,16 @@ __global__ __launch_bounds__(256) void amax_kernel(const T *__restrict__ x, int6
                                                    float *__restrict__ partials) {
     float m = 0.0f;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < n8; u += stride) {
-        float v[8];
-        load8(x + u * 8, v);
+    for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < n8; u += 4 * stride) {
+        float v[4][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+        for (int k = 0; k < 4; ++k)
+            if (u + k * stride < n8) load8(x + (u + k * stride) * 8, v[k]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (u + k * stride < n8)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[k][i]));
     }
     m = wave_max(m);
     __shared__ float red[4];
@@ -132,27 +137,36 @@ __device__ __forceinline__ void encode_half_block(const float (&x)[8], float s_e
 }
 
 // ---------------------------------------------------------------------------
-// 1-D encode: units of 8 elements; the total is a multiple of 16
+// 1-D encode: one lane per 1x16 block, two blocks in flight per lane
 // ---------------------------------------------------------------------------
 
 template <typename T, bool FOUR_OVER_SIX>
 __global__ __launch_bounds__(256) void encode1d_kernel(
-    const T *__restrict__ x, int64_t n8, const float *__restrict__ partials, int np,
-    const float *__restrict__ amax_in, uint32_t *__restrict__ codes,
-    uint8_t *__restrict__ scales, float *__restrict__ s_dec_out) {
+    const T *__restrict__ x, int64_t nblk, const float *__restrict__ partials, int np,
+    const float *__restrict__ amax_in, uint2 *__restrict__ codes, uint8_t *__restrict__ scales,
+    float *__restrict__ s_dec_out) {
     __shared__ f32x2 lut[128];
     float s_enc;
     encode_prologue(partials, np, amax_in, s_dec_out, lut, s_enc);
+    typedef typename Raw16Of<T>::type Raw;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    // The trip count is uniform across each lane pair (stride and start are even),
-    // so both halves of a block are always processed together.
-    for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < n8; u += stride) {
-        float v[8];
-        load8(x + u * 8, v);
-        uint32_t q, sc;
-        encode_half_block<FOUR_OVER_SIX>(v, s_enc, lut, q, sc);
-        codes[u] = q;
-        if ((u & 1) == 0) scales[u >> 1] = (uint8_t)sc;
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += 2 * stride) {
+        const int64_t b2 = b + stride;
+        Raw r0, r1;
+        load_raw16(x + b * 16, r0);
+        if (b2 < nblk) load_raw16(x + b2 * 16, r1);
+        float v[16];
+        uint32_t lo, hi, sc;
+        unpack16(r0, v);
+        encode_block16<FOUR_OVER_SIX>(v, s_enc, lut, lo, hi, sc);
+        codes[b] = make_uint2(lo, hi);
+        scales[b] = (uint8_t)sc;
+        if (b2 < nblk) {
+            unpack16(r1, v);
+            encode_block16<FOUR_OVER_SIX>(v, s_enc, lut, lo, hi, sc);
+            codes[b2] = make_uint2(lo, hi);
+            scales[b2] = (uint8_t)sc;
+        }
     }
 }
 
@@ -215,27 +229,27 @@ __global__ __launch_bounds__(256) void encode2d_kernel(
 // ---------------------------------------------------------------------------
 
 template <typename TOUT, bool TWO_D>
-__global__ __launch_bounds__(256) void dequant_kernel(const uint32_t *__restrict__ codes,
+__global__ __launch_bounds__(256) void dequant_kernel(const uint2 *__restrict__ codes,
                                                       const uint8_t *__restrict__ scales,
                                                       const float *__restrict__ s_dec_p,
-                                                      int64_t n8, int64_t cols,
+                                                      int64_t nblk, int64_t cols,
                                                       TOUT *__restrict__ y) {
     const float s_dec = *s_dec_p;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const int64_t tcols = cols >> 4;
-    for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < n8; u += stride) {
-        int64_t si;
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += stride) {
+        int64_t si = b;
         if (TWO_D) {
-            const int64_t e0 = u * 8;
-            const int64_t row = e0 / cols, col = e0 - row * cols;
-            si = (row >> 4) * tcols + (col >> 4);
-        } else {
-            si = u >> 1;
+            const int64_t row = b / tcols, cb = b - row * tcols;
+            si = (row >> 4) * tcols + cb;
         }
+        const uint2 q = codes[b];
         const float S = e4m3_value(scales[si]) * s_dec;
         float v[8];
-        dequant8(codes[u], S, v);
-        store8(y + u * 8, v);
+        dequant8(q.x, S, v);
+        store8(y + b * 16, v);
+        dequant8(q.y, S, v);
+        store8(y + b * 16 + 8, v);
     }
 }
 
@@ -264,6 +278,10 @@ hipError_t launch_amax(const void *x, int dtype, int64_t n, float *partials, int
 
 int amax_partials_for(int64_t n) { return grid_for(n / 8, 256 * 4, kMaxPartials); }
 
+// Workgroups of the streaming kernels: enough to fill every CU several
+// times, few enough that the per-workgroup prologue stays small.
+constexpr int kStreamGrid = 1024;
+
 hipError_t launch_encode(const void *x, int dtype, int64_t rows, int64_t cols, int layout,
                          int search, const float *partials, int np, const float *amax_in,
                          uint8_t *codes, uint8_t *scales, float *s_dec, hipStream_t s) {
@@ -271,11 +289,12 @@ hipError_t launch_encode(const void *x, int dtype, int64_t rows, int64_t cols, i
     const bool f46 = (search == 1);
     uint32_t *c32 = (uint32_t *)codes;
     if (layout == 0) {
-        const int64_t n8 = n / 8;
-        const int g = grid_for(n8, 256 * 4, 8192);
+        const int64_t nblk = n / 16;
+        const int g = grid_for(nblk, 256, kStreamGrid);
+        uint2 *c64 = (uint2 *)codes;
 #define L1(T, F)                                                                          \
     NVFP4_LAUNCH("encode1d", (encode1d_kernel<T, F>), dim3(g), dim3(256), 0, s, (const T *)x, \
-                 n8, partials, np, amax_in, c32, scales, s_dec)
+                 nblk, partials, np, amax_in, c64, scales, s_dec)
         if (dtype == kF32) {
             if (f46) L1(float, true); else L1(float, false);
         } else {
@@ -301,12 +320,12 @@ hipError_t launch_encode(const void *x, int dtype, int64_t rows, int64_t cols, i
 hipError_t launch_dequant(const uint8_t *codes, const uint8_t *scales, const float *s_dec,
                           int64_t rows, int64_t cols, int layout, void *y, int ydtype,
                           hipStream_t s) {
-    const int64_t n8 = rows * cols / 8;
-    const int g = grid_for(n8, 256 * 4, 8192);
-    const uint32_t *c32 = (const uint32_t *)codes;
+    const int64_t nblk = rows * cols / 16;
+    const int g = grid_for(nblk, 256 * 2, 8192);
+    const uint2 *c64 = (const uint2 *)codes;
 #define LD(T, TWO)                                                                     \
-    NVFP4_LAUNCH("dequant", (dequant_kernel<T, TWO>), dim3(g), dim3(256), 0, s, c32, scales, \
-                 s_dec, n8, cols, (T *)y)
+    NVFP4_LAUNCH("dequant", (dequant_kernel<T, TWO>), dim3(g), dim3(256), 0, s, c64, scales, \
+                 s_dec, nblk, cols, (T *)y)
     if (ydtype == kF32) {
         if (layout) LD(float, true); else LD(float, false);
     } else {

@@ -313,22 +313,31 @@ void orc_to_bf16(const float *x, int64_t n, uint16_t *out)
 /* Per-channel mean of the chunk's keys ([DR] inference: keys are
  * K-smoothed before NVFP4 quantization; the pages give no formula, READING:
  * subtract the per-channel mean over the chunk's tokens).  K is [T, HD]
- * (HD = heads * head_dim, token-major).  Sum in double: tokens are taken in
- * tiles of 64, each tile summed in token order, the tile sums added in tile
- * order; mu = (float)(S / T). */
+ * (HD = heads * head_dim, token-major).  The sum is taken in double, in a
+ * fixed order (READING; the pages fix none): tokens in tiles of 16, each
+ * tile summed in token order from +0; the tile sums, padded with zeros to a
+ * power-of-two count, added pairwise level by level (adjacent pairs);
+ * mu = (float)(S / T). */
 void orc_kv_mean(const float *K, int64_t T, int64_t HD, float *mu)
 {
+    const int64_t ntiles = (T + 15) / 16;
+    int64_t npad = 1;
+    while (npad < ntiles)
+        npad *= 2;
+    double *tile = (double *)malloc((size_t)npad * sizeof(double) + 1);
     for (int64_t ch = 0; ch < HD; ++ch) {
-        double S = 0.0;
-        for (int64_t p0 = 0; p0 < T; p0 += 64) {
-            int64_t p1 = (p0 + 64 < T) ? p0 + 64 : T;
+        for (int64_t p = 0; p < npad; ++p) {
             double P = 0.0;
-            for (int64_t t = p0; t < p1; ++t)
+            for (int64_t t = 16 * p; t < 16 * p + 16 && t < T; ++t)
                 P += (double)K[t * HD + ch];
-            S += P;
+            tile[p] = P;
         }
-        mu[ch] = (T > 0) ? (float)(S / (double)T) : 0.0f;
+        for (int64_t n = npad; n > 1; n /= 2)
+            for (int64_t i = 0; i < n / 2; ++i)
+                tile[i] = tile[2 * i] + tile[2 * i + 1];
+        mu[ch] = (T > 0) ? (float)(tile[0] / (double)T) : 0.0f;
     }
+    free(tile);
 }
 
 /* Quantize one KV chunk independently ([DR]: chunk-level, F_c = 8 frames;
