@@ -98,6 +98,19 @@ __device__ __forceinline__ float half_block_error(const float (&x)[8], uint32_t 
     return acc;
 }
 
+// RN(a / 6) for a >= 0.  For a >= 2^-125, q = RN(a * RN(1/6)) corrected once
+// by the exact residual fma(-q, 6, a) is the correctly rounded quotient
+// (checked exhaustively over every float in [2^-125, FLT_MAX]); smaller a
+// (quotient near or below the subnormal range) takes the IEEE division.
+__device__ __forceinline__ float div6_rn(float a) {
+    const float c = 0.16666667f;  // RN(1/6)
+    const float q0 = a * c;
+    const float r = __builtin_fmaf(-q0, 6.0f, a);
+    float q = __builtin_fmaf(r, c, q0);
+    if (a < 0x1p-125f) q = a / 6.0f;
+    return q;
+}
+
 // ---------------------------------------------------------------------------
 // one 1x16 block held by one lane: the Four-Over-Six encoder
 // ---------------------------------------------------------------------------
@@ -124,7 +137,7 @@ __device__ __forceinline__ void encode_block16(const float (&x)[16], float s_enc
     float am = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(x[i]));
-    const uint32_t sc6 = e4m3_encode((am / 6.0f) * s_enc);
+    const uint32_t sc6 = e4m3_encode(div6_rn(am) * s_enc);
     const f32x2 sr6 = lut[sc6];
     const uint32_t a6 = e2m1_pack8(xl, sr6.y), b6 = e2m1_pack8(xh, sr6.y);
     if (!FOUR_OVER_SIX) {

@@ -35,7 +35,7 @@ namespace nvfp4 {
 // workgroup = 4 waves = 4 consecutive tiles); kv_finalize finishes the tree.
 constexpr int kSeq = 16;            // tokens summed sequentially by one lane
 constexpr int kStatsTokens = 64;    // tokens per stats workgroup (4 waves x 16)
-constexpr int kGroupCh = 512;       // channels per stats workgroup (64 lanes x 8)
+constexpr int kGroupCh = 256;       // channels per stats workgroup (64 lanes x 4)
 constexpr int kFinCh = 64;          // channels per finalize workgroup
 
 struct KvWs {
@@ -89,8 +89,8 @@ size_t kv_store_ws_bytes(int64_t T, int64_t HD) {
                     align256(d.nt64 * d.gy * 4) + align256(d.nfin * 4));
 }
 
-// Workgroup (tile p of 64 tokens, channel group g of 512, blockIdx.z = 0):
-// wave w sums tokens 64p + 16w .. +15 of its lane's 8 channels sequentially;
+// Workgroup (tile p of 64 tokens, channel group g of 256, blockIdx.z = 0):
+// wave w sums tokens 64p + 16w .. +15 of its lane's 4 channels sequentially;
 // the four wave sums are combined as ((s0 + s1) + (s2 + s3)); key max/min
 // per channel.  blockIdx.z = 1 workgroups take the value |max| of the same
 // tile.  Loads are unconditional (token index clamped) so that all 16 of a
@@ -106,28 +106,25 @@ __global__ __launch_bounds__(256) void kv_stats_kernel(const uint16_t *__restric
     __shared__ float svm[4];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t p = blockIdx.x;
-    const int chl = lane * 8;
+    const int chl = lane * 4;
     const int64_t chq = (int64_t)blockIdx.y * kGroupCh + chl;
     const bool ch_ok = chq < HD;
     const int64_t ch0 = ch_ok ? chq : 0;
     const int64_t t0 = p * kStatsTokens + wave * kSeq;
-    u32x4 r[kSeq];
+    uint2 r[kSeq];
     const uint16_t *src = blockIdx.z ? V : K;
 #pragma unroll
     for (int j = 0; j < kSeq; ++j) {
         const int64_t t = (t0 + j < T) ? t0 + j : T - 1;
-        r[j] = *(const u32x4 *)(src + t * HD + ch0);
+        r[j] = *(const uint2 *)(src + t * HD + ch0);
     }
     if (blockIdx.z) {
         float vmx = 0.0f;
 #pragma unroll
         for (int j = 0; j < kSeq; ++j) {
             const bool ok = ch_ok && (t0 + j < T);
-            const uint32_t vw[4] = {r[j].x, r[j].y, r[j].z, r[j].w};
-            float m = 0.0f;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                m = fmaxf(m, fmaxf(fabsf(bf16lo(vw[q])), fabsf(bf16hi(vw[q]))));
+            const float m = fmaxf(fmaxf(fabsf(bf16lo(r[j].x)), fabsf(bf16hi(r[j].x))),
+                                  fmaxf(fabsf(bf16lo(r[j].y)), fabsf(bf16hi(r[j].y))));
             vmx = ok ? fmaxf(vmx, m) : vmx;
         }
         vmx = wave_max(vmx);
@@ -138,10 +135,10 @@ __global__ __launch_bounds__(256) void kv_stats_kernel(const uint16_t *__restric
                 fmaxf(fmaxf(svm[0], svm[1]), fmaxf(svm[2], svm[3]));
         return;
     }
-    double s[8];
-    float mx[8], mn[8];
+    double s[4];
+    float mx[4], mn[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
         s[i] = 0.0;
         mx[i] = -__builtin_huge_valf();
         mn[i] = __builtin_huge_valf();
@@ -149,26 +146,23 @@ __global__ __launch_bounds__(256) void kv_stats_kernel(const uint16_t *__restric
 #pragma unroll
     for (int j = 0; j < kSeq; ++j) {
         const bool ok = t0 + j < T;
-        const uint32_t kw[4] = {r[j].x, r[j].y, r[j].z, r[j].w};
+        const float v[4] = {bf16lo(r[j].x), bf16hi(r[j].x), bf16lo(r[j].y), bf16hi(r[j].y)};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float a = bf16lo(kw[q]), b = bf16hi(kw[q]);
-            s[2 * q] += ok ? (double)a : 0.0;
-            s[2 * q + 1] += ok ? (double)b : 0.0;
-            mx[2 * q] = ok ? fmaxf(mx[2 * q], a) : mx[2 * q];
-            mx[2 * q + 1] = ok ? fmaxf(mx[2 * q + 1], b) : mx[2 * q + 1];
-            mn[2 * q] = ok ? fminf(mn[2 * q], a) : mn[2 * q];
-            mn[2 * q + 1] = ok ? fminf(mn[2 * q + 1], b) : mn[2 * q + 1];
+        for (int i = 0; i < 4; ++i) {
+            s[i] += ok ? (double)v[i] : 0.0;
+            mx[i] = ok ? fmaxf(mx[i], v[i]) : mx[i];
+            mn[i] = ok ? fminf(mn[i], v[i]) : mn[i];
         }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
         sp[wave][chl + i] = s[i];
         smx[wave][chl + i] = mx[i];
         smn[wave][chl + i] = mn[i];
     }
     __syncthreads();
-    for (int c = threadIdx.x; c < kGroupCh; c += blockDim.x) {
+    {
+        const int c = threadIdx.x;  // 256 threads, 256 channels
         const int64_t ch = (int64_t)blockIdx.y * kGroupCh + c;
         if (ch < HD) {
             const double P = (sp[0][c] + sp[1][c]) + (sp[2][c] + sp[3][c]);
@@ -314,9 +308,12 @@ __global__ __launch_bounds__(256) void kv_encode_kernel(
     // channel of the block's first element, advanced without division: (16 b) mod HD
     int64_t ch0 = (b * 16) % HD;
     const int64_t step = (stride * 16) % HD;
+    Raw16Bf16 rn;
+    if (b < nblk) load_raw16(x + b * 16, rn);
     for (; b < nblk; b += stride) {
-        Raw16Bf16 r;
-        load_raw16(x + b * 16, r);
+        // the next block's load is issued before this block is encoded
+        const Raw16Bf16 r = rn;
+        if (b + stride < nblk) load_raw16(x + (b + stride) * 16, rn);
         float v[16];
         unpack16(r, v);
         if (which == 0) {

@@ -99,7 +99,7 @@ template <int TARGET>
 __device__ __forceinline__ void candidate(const float (&x)[8], float am, float s_enc,
                                           const f32x2 *lut, uint32_t &sc, uint32_t &q,
                                           float &err_half) {
-    float ideal = (TARGET == 6) ? (am / 6.0f) * s_enc : (am * 0.25f) * s_enc;
+    float ideal = (TARGET == 6) ? div6_rn(am) * s_enc : (am * 0.25f) * s_enc;
     sc = e4m3_encode(ideal);
     f32x2 sr = lut[sc];
     q = e2m1_pack8(x, sr.y);

@@ -100,6 +100,16 @@ def test_quantize_wide_dynamic_range(nv, orc):
     check_quant(nv, orc, x, torch.float32, 0, 0)
 
 
+def test_quantize_subnormal_blocks(nv, orc):
+    # blocks of subnormal values next to normal ones: block amax below 2^-125
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((256, 128)).astype(np.float32)
+    x[::3, :64] = (rng.standard_normal((86, 64)) * 1e-39).astype(np.float32)
+    x[1::5, 64:80] = np.float32(2.0 ** -149)
+    check_quant(nv, orc, x, torch.float32, 0, 1)
+    check_quant(nv, orc, x, torch.float32, 1, 1)
+
+
 def test_quantize_empty(nv):
     x = torch.empty((0, 32), dtype=torch.bfloat16, device="cuda")
     q = nv.quantize(x)
