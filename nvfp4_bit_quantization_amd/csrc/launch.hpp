@@ -2,6 +2,7 @@
 // Arguments are validated by the C ABI layer (capi.cpp) before these run.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -9,17 +10,20 @@ namespace nvfp4 {
 
 // ---- profile.cpp: optional HIP-event timing of every launch
 bool prof_on();
-int prof_begin(const char *name, hipStream_t s);
-void prof_end(int idx, hipStream_t s);
+// Reserves a (start, stop) event pair under NAME; false if none is available.
+bool prof_take(const char *name, hipEvent_t *start, hipEvent_t *stop);
 
-// Launch KERNEL (parenthesise template kernels) and, when timing is enabled,
-// bracket it with events recorded on the same stream under NAME.
-#define NVFP4_LAUNCH(NAME, KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)               \
-    do {                                                                         \
-        const bool _p = ::nvfp4::prof_on();                                      \
-        const int _i = _p ? ::nvfp4::prof_begin(NAME, STREAM) : -1;             \
-        hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);     \
-        if (_p) ::nvfp4::prof_end(_i, STREAM);                                   \
+// Launch KERNEL (parenthesise template kernels).  When timing is enabled the
+// launch goes through hipExtLaunchKernelGGL with an event pair that the
+// dispatch itself time-stamps at kernel start and end, on STREAM.
+#define NVFP4_LAUNCH(NAME, KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                       \
+    do {                                                                                 \
+        hipEvent_t _e0 = nullptr, _e1 = nullptr;                                         \
+        if (::nvfp4::prof_on() && ::nvfp4::prof_take(NAME, &_e0, &_e1))                  \
+            hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, _e0, _e1, 0,       \
+                                  __VA_ARGS__);                                          \
+        else                                                                             \
+            hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);         \
     } while (0)
 
 constexpr int kF32 = 0;

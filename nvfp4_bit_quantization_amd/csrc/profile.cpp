@@ -1,9 +1,11 @@
 // profile.cpp -- kernel timing for libnvfp4 (tracing).
 //
-// While enabled, every kernel launch of the library is bracketed by two HIP
-// events recorded on the launch's own stream; nvfp4_profile_collect()
-// waits for the recorded events and returns, per kernel name, the number of
-// launches and the summed event-to-event milliseconds.  Events are created
+// While enabled, every kernel launch of the library carries two HIP events
+// that the dispatch packet itself time-stamps at kernel start and end
+// (hipExtLaunchKernelGGL, on the launch's own stream), so the interval is the
+// kernel's execution alone; nvfp4_profile_collect() waits for the events and
+// returns, per kernel name, the number of launches and the summed
+// milliseconds.  Events are created
 // lazily and reused; nothing is allocated on the device.  Disabled by
 // default, and free when disabled (one relaxed atomic load per launch).
 #include "../../include/nvfp4.h"
@@ -46,19 +48,18 @@ hipEvent_t take_event() {
 
 bool prof_on() { return g_on.load(std::memory_order_relaxed) != 0; }
 
-int prof_begin(const char *name, hipStream_t s) {
+bool prof_take(const char *name, hipEvent_t *start, hipEvent_t *stop) {
     std::lock_guard<std::mutex> lk(g_mu);
     Mark m{name, take_event(), take_event()};
-    if (!m.start || !m.stop) return -1;
-    if (hipEventRecord(m.start, s) != hipSuccess) return -1;
+    if (!m.start || !m.stop) {
+        if (m.start) g_free.push_back(m.start);
+        if (m.stop) g_free.push_back(m.stop);
+        return false;
+    }
     g_marks.push_back(m);
-    return (int)g_marks.size() - 1;
-}
-
-void prof_end(int idx, hipStream_t s) {
-    if (idx < 0) return;
-    std::lock_guard<std::mutex> lk(g_mu);
-    if (idx < (int)g_marks.size()) (void)hipEventRecord(g_marks[idx].stop, s);
+    *start = m.start;
+    *stop = m.stop;
+    return true;
 }
 
 }  // namespace nvfp4
