@@ -22,10 +22,15 @@ namespace nvfp4 {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Word 3 of a raw (untyped) buffer descriptor on CDNA: 32-bit data format,
+// no swizzle, no index stride.
+constexpr int kBufferWord3 = 0x00020000;
 
 // Largest E2M1 magnitude times largest E4M3 magnitude: the tensor amax maps to it.
 constexpr float kTensorTarget = 2688.0f;  // 6 * 448

@@ -12,17 +12,20 @@
 // uses micro-block scaling with the Four Over Six selection.
 //
 // Store = three launches:
-//   kv_stats     one wave per (64-token tile, 512 channels): per-channel fp64
-//                tile sums (token order), key max/min, value |max|
-//   kv_finalize  one workgroup: mu = (float)(sum of tile sums / T), the key
-//                amax max_c max(RN(max K - mu), RN(mu - min K)) (equal to the
-//                elementwise amax of RN(K - mu) because RN is monotone), the
-//                value amax, and the FP32 tensor scales of K_s and V
-//   kv_encode    the 1-D 4/6 encoder over K_s = RN(K - mu) and V, writing the
-//                ring slot and, for sink chunks, the sink copy in the same pass
-// Gather = one launch: one workgroup-iteration per output token, one lane per
-// 8 elements; each token's segment (ring slot or sink copy) is found by a
-// scalar scan of <= W + 2 segments.
+//   kv_stats     two waves per (64-token node, 512 channels): per-channel fp64
+//                tile sums (token order) combined up to the 64-token node,
+//                key max/min, value |max|
+//   kv_finalize  one wave per 16 channels: mu = (float)(sum of tile sums / T)
+//                by the pairwise tree, and the key amax
+//                max_c max(RN(max K - mu), RN(mu - min K)) (equal to the
+//                elementwise amax of RN(K - mu) because RN is monotone)
+//   kv_encode    reduces the amax partials to the FP32 tensor scales of K_s
+//                and V, then the 1-D 4/6 encoder over K_s = RN(K - mu) and V,
+//                writing the ring slot and, for sink chunks, the sink copy in
+//                the same pass
+// Gather = one launch: one workgroup-iteration per kGatherTok output tokens,
+// one lane per 16-element block; each token's segment (ring slot or sink
+// copy) is found from scalars (sink lengths, window start, W).
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -32,25 +35,26 @@ namespace nvfp4 {
 // tiles of kSeq = 16, each tile summed in token order in double; the tile
 // sums, padded with zeros to a power-of-two count, added pairwise level by
 // level.  kv_stats computes the tile sums and the first two tree levels (one
-// workgroup = 4 waves = 4 consecutive tiles); kv_finalize finishes the tree.
+// workgroup = 2 waves = 4 consecutive tiles); kv_finalize finishes the tree.
 constexpr int kSeq = 16;            // tokens summed sequentially by one lane
-constexpr int kStatsTokens = 64;    // tokens per stats workgroup (4 waves x 16)
-constexpr int kGroupCh = 256;       // channels per stats workgroup (64 lanes x 4)
-constexpr int kFinCh = 64;          // channels per finalize workgroup
+constexpr int kStatsTokens = 64;    // tokens per stats unit (4 tiles of 16)
+constexpr int kGroupCh = 512;       // channels per stats unit (64 lanes x 8)
+constexpr int kFinCh = 16;          // channels per finalize wave
+constexpr int64_t kEncodeGrid = 512; // encode workgroups per tensor (upper bound)
 
 struct KvWs {
     double *P;      // [nt64, HD]  level-2 tree nodes (64-token sums)
     float *kmax;    // [nt64, HD]
     float *kmin;    // [nt64, HD]
-    float *vpart;   // [nt64 * gy] value |max| per stats workgroup
-    float *kpart;   // [nfin]      key amax per finalize workgroup
+    float *vpart;   // [nt64 * gy] value |max| per stats unit
+    float *kpart;   // [nfin]      key amax per finalize wave
 };
 
 struct KvDims {
-    int64_t nt64;   // stats workgroups along tokens
-    int64_t gy;     // stats workgroups along channels
+    int64_t nt64;   // stats units along tokens (64-token nodes)
+    int64_t gy;     // stats units along channels
     int64_t n2;     // level-2 nodes in the padded tree (power of two)
-    int64_t nfin;   // finalize workgroups
+    int64_t nfin;   // finalize waves (one workgroup each)
 };
 
 static inline int64_t align256(int64_t b) { return (b + 255) & ~(int64_t)255; }
@@ -89,88 +93,161 @@ size_t kv_store_ws_bytes(int64_t T, int64_t HD) {
                     align256(d.nt64 * d.gy * 4) + align256(d.nfin * 4));
 }
 
-// Workgroup (tile p of 64 tokens, channel group g of 256, blockIdx.z = 0):
-// wave w sums tokens 64p + 16w .. +15 of its lane's 4 channels sequentially;
-// the four wave sums are combined as ((s0 + s1) + (s2 + s3)); key max/min
-// per channel.  blockIdx.z = 1 workgroups take the value |max| of the same
-// tile.  Loads are unconditional (token index clamped) so that all 16 of a
-// lane's loads are in flight together; out-of-range tokens contribute +0 to
-// the sums (no partial sum is -0, so adding +0 changes nothing) and nothing
-// to the extrema.
-__global__ __launch_bounds__(256) void kv_stats_kernel(const uint16_t *__restrict__ K,
-                                                       const uint16_t *__restrict__ V, int64_t T,
-                                                       int64_t HD, KvWs w) {
-    __shared__ double sp[4][kGroupCh];
-    __shared__ float smx[4][kGroupCh];
-    __shared__ float smn[4][kGroupCh];
-    __shared__ float svm[4];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t p = blockIdx.x;
-    const int chl = lane * 4;
-    const int64_t chq = (int64_t)blockIdx.y * kGroupCh + chl;
-    const bool ch_ok = chq < HD;
-    const int64_t ch0 = ch_ok ? chq : 0;
-    const int64_t t0 = p * kStatsTokens + wave * kSeq;
-    uint2 r[kSeq];
-    const uint16_t *src = blockIdx.z ? V : K;
+constexpr int kHalf = kStatsTokens / 2;  // tokens per stats wave (two tiles)
+
+// The 32 loads of a wave's two tiles (a full node: no token past T) as raw
+// buffer loads: the node's wave-uniform base is in the buffer descriptor,
+// the token's byte offset in a scalar register and the lane's byte offset in
+// one vector register shared by all loads.
+__device__ __forceinline__ void stats_load(u32x4 (&r)[kHalf], __amdgpu_buffer_rsrc_t rs,
+                                           uint32_t voff, uint32_t tok0, uint32_t row_bytes) {
 #pragma unroll
-    for (int j = 0; j < kSeq; ++j) {
-        const int64_t t = (t0 + j < T) ? t0 + j : T - 1;
-        r[j] = *(const uint2 *)(src + t * HD + ch0);
+    for (int j = 0; j < kHalf; ++j)
+        r[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (tok0 + j) * row_bytes, 0);
+}
+
+__device__ __forceinline__ void bf16x8(const u32x4 &r, float (&v)[8]) {
+    v[0] = bf16lo(r.x);
+    v[1] = bf16hi(r.x);
+    v[2] = bf16lo(r.y);
+    v[3] = bf16hi(r.y);
+    v[4] = bf16lo(r.z);
+    v[5] = bf16hi(r.z);
+    v[6] = bf16lo(r.w);
+    v[7] = bf16hi(r.w);
+}
+
+// Key token: add to the running per-channel sums (double), max / min.
+__device__ __forceinline__ void stats_key_token(const u32x4 &r, double (&s)[8], float (&mx)[8],
+                                                float (&mn)[8]) {
+    float v[8];
+    bf16x8(r, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        s[i] += (double)v[i];
+        mx[i] = fmaxf(mx[i], v[i]);
+        mn[i] = fminf(mn[i], v[i]);
+        // the extrema are materialised token by token: otherwise the max / min
+        // chains get regrouped across tokens and keep every value alive
+        asm volatile("" : "+v"(mx[i]), "+v"(mn[i]));
     }
-    if (blockIdx.z) {
-        float vmx = 0.0f;
+}
+
+__device__ __forceinline__ float stats_value_token(const u32x4 &r, float m) {
+    float v[8];
+    bf16x8(r, v);
 #pragma unroll
-        for (int j = 0; j < kSeq; ++j) {
-            const bool ok = ch_ok && (t0 + j < T);
-            const float m = fmaxf(fmaxf(fabsf(bf16lo(r[j].x)), fabsf(bf16hi(r[j].x))),
-                                  fmaxf(fabsf(bf16lo(r[j].y)), fabsf(bf16hi(r[j].y))));
-            vmx = ok ? fmaxf(vmx, m) : vmx;
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+    return m;
+}
+
+// Workgroup = 2 waves = one unit (64-token node p, 512-channel group y);
+// blockIdx.y selects keys (0) or values (1).  Wave h takes tokens
+// 64 p + 32 h .. +31; lane l owns channels 512 y + 8 l .. +7 (one 16-byte
+// load per token), and all 32 loads of a wave are issued before any is
+// used.  Keys: each 16-token tile is summed in token order in double; the
+// wave adds its two tile sums (tree level 1), wave 1 hands its node to wave
+// 0 through LDS, which adds them (level 2) and stores the level-2 node with
+// the per-channel max / min.  Values: the |max| of the unit.  The last,
+// partial node reads token by token up to T; its absent tiles are +0, the
+// value the padded tree gives them.
+__global__ __launch_bounds__(128) void kv_stats_kernel(const uint16_t *__restrict__ K,
+                                                       const uint16_t *__restrict__ V, int64_t T,
+                                                       int64_t HD, int64_t gy, KvWs w) {
+    __shared__ double sp[8][64];
+    __shared__ float sx[8][64];
+    __shared__ float sn[8][64];
+    __shared__ float sv;
+    const int h = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int64_t unit = blockIdx.x;
+    const int64_t p = unit / gy, y = unit - p * gy;
+    const int64_t chq = y * kGroupCh + lane * 8;
+    const bool ch_ok = chq < HD;  // HD is a multiple of 16: all 8 channels or none
+    const uint32_t off = ch_ok ? (uint32_t)lane * 8 : 0u;
+    const int64_t t0 = p * kStatsTokens + h * kHalf;
+    const uint16_t *row = (blockIdx.y ? V : K) + y * kGroupCh + t0 * HD;  // wave-uniform
+    const bool full = t0 + kHalf <= T;
+    // descriptor over the wave's rows (32 * HD * 2 bytes < 2^32: HD < 2^26)
+    const uint32_t rb = (uint32_t)HD * 2, voff = off * 2;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)row, (short)0, (int)(kHalf * rb), kBufferWord3);
+    if (blockIdx.y) {
+        float m = 0.0f;
+        if (full) {
+            u32x4 r[kHalf];
+            stats_load(r, rs, voff, 0, rb);
+#pragma unroll
+            for (int j = 0; j < kHalf; ++j) m = stats_value_token(r[j], m);
+        } else {
+#pragma unroll 1
+            for (int64_t j = 0; t0 + j < T; ++j)
+                m = stats_value_token(*(const u32x4 *)(row + j * HD + off), m);
         }
-        vmx = wave_max(vmx);
-        if (lane == 0) svm[wave] = vmx;
+        m = ch_ok ? m : 0.0f;
+        m = wave_max(m);
+        if (h == 1 && lane == 0) sv = m;
         __syncthreads();
-        if (threadIdx.x == 0)
-            w.vpart[p * gridDim.y + blockIdx.y] =
-                fmaxf(fmaxf(svm[0], svm[1]), fmaxf(svm[2], svm[3]));
+        if (h == 0 && lane == 0) w.vpart[unit] = fmaxf(m, sv);
         return;
     }
-    double s[4];
-    float mx[4], mn[4];
+    double node[8];
+    float mx[8], mn[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        s[i] = 0.0;
+    for (int i = 0; i < 8; ++i) {
         mx[i] = -__builtin_huge_valf();
         mn[i] = __builtin_huge_valf();
     }
+    if (full) {
+        u32x4 r[kHalf];
+        stats_load(r, rs, voff, 0, rb);
+        double a[8], b[8];
 #pragma unroll
-    for (int j = 0; j < kSeq; ++j) {
-        const bool ok = t0 + j < T;
-        const float v[4] = {bf16lo(r[j].x), bf16hi(r[j].x), bf16lo(r[j].y), bf16hi(r[j].y)};
+        for (int i = 0; i < 8; ++i) a[i] = b[i] = 0.0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            s[i] += ok ? (double)v[i] : 0.0;
-            mx[i] = ok ? fmaxf(mx[i], v[i]) : mx[i];
-            mn[i] = ok ? fminf(mn[i], v[i]) : mn[i];
-        }
+        for (int j = 0; j < kSeq; ++j) stats_key_token(r[j], a, mx, mn);
+#pragma unroll
+        for (int j = kSeq; j < kHalf; ++j) stats_key_token(r[j], b, mx, mn);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) node[i] = a[i] + b[i];
+    } else {
+        double a[8], b[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] = b[i] = 0.0;
+#pragma unroll 1
+        for (int64_t j = 0; j < kSeq && t0 + j < T; ++j)
+            stats_key_token(*(const u32x4 *)(row + j * HD + off), a, mx, mn);
+#pragma unroll 1
+        for (int64_t j = kSeq; j < kHalf && t0 + j < T; ++j)
+            stats_key_token(*(const u32x4 *)(row + j * HD + off), b, mx, mn);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) node[i] = a[i] + b[i];
     }
+    if (h == 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        sp[wave][chl + i] = s[i];
-        smx[wave][chl + i] = mx[i];
-        smn[wave][chl + i] = mn[i];
+        for (int i = 0; i < 8; ++i) {
+            sp[i][lane] = node[i];
+            sx[i][lane] = mx[i];
+            sn[i][lane] = mn[i];
+        }
     }
     __syncthreads();
-    {
-        const int c = threadIdx.x;  // 256 threads, 256 channels
-        const int64_t ch = (int64_t)blockIdx.y * kGroupCh + c;
-        if (ch < HD) {
-            const double P = (sp[0][c] + sp[1][c]) + (sp[2][c] + sp[3][c]);
-            w.P[p * HD + ch] = P;
-            w.kmax[p * HD + ch] = fmaxf(fmaxf(smx[0][c], smx[1][c]), fmaxf(smx[2][c], smx[3][c]));
-            w.kmin[p * HD + ch] = fminf(fminf(smn[0][c], smn[1][c]), fminf(smn[2][c], smn[3][c]));
-        }
+    if (h == 1 || !ch_ok) return;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        node[i] = node[i] + sp[i][lane];
+        mx[i] = fmaxf(mx[i], sx[i][lane]);
+        mn[i] = fminf(mn[i], sn[i][lane]);
     }
+    double *P = w.P + p * HD + chq;
+    float *X = w.kmax + p * HD + chq;
+    float *N = w.kmin + p * HD + chq;
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) *(f64x2 *)(P + i) = f64x2{node[i], node[i + 1]};
+    *(f32x4 *)X = f32x4{mx[0], mx[1], mx[2], mx[3]};
+    *(f32x4 *)(X + 4) = f32x4{mx[4], mx[5], mx[6], mx[7]};
+    *(f32x4 *)N = f32x4{mn[0], mn[1], mn[2], mn[3]};
+    *(f32x4 *)(N + 4) = f32x4{mn[4], mn[5], mn[6], mn[7]};
 }
 
 // Tree sum of 32 doubles, adjacent pairs level by level.
@@ -182,26 +259,26 @@ __device__ __forceinline__ double tree32(double (&v)[32]) {
     return v[0];
 }
 
-// Workgroup of 256 threads = 4 waves over 64 channels (lane = channel).  The
-// level-2 nodes of a channel form blocks of 32 (nodes past the last 64-token
-// tile are zero); wave q sums blocks q, q+4, ... with a fixed 32-leaf tree
-// into LDS, then wave 0 sums the block sums with the same tree (zero padded;
-// adding an exact zero changes nothing, and no partial sum is -0).  This is
-// the level-by-level pairwise tree over the 16-token tile sums.
-// mu = (float)(S / T); the workgroup's key amax
-// max_c max(RN(max K - mu), RN(mu - min K)) goes to kpart.
-__global__ __launch_bounds__(256) void kv_finalize_kernel(KvWs w, int64_t nt64, int64_t n2,
-                                                          int64_t T, int64_t HD, float *mu_slot,
-                                                          float *mu_g, float *mu_s) {
+// One wave per 16 channels: lane = (channel c = lane & 15, quarter
+// q = lane >> 4).  The level-2 nodes of a channel form blocks of 32 (nodes
+// past the last 64-token node are zero); quarter q sums blocks q, q + 4, ...
+// with a fixed 32-leaf tree into LDS, then the q = 0 lanes sum the block
+// sums with the same tree (zero padded; adding an exact zero changes
+// nothing, and no partial sum is -0).  This is the level-by-level pairwise
+// tree over the 16-token tile sums.  mu = (float)(S / T); the wave's key
+// amax max_c max(RN(max K - mu), RN(mu - min K)) goes to kpart.
+__global__ __launch_bounds__(64) void kv_finalize_kernel(KvWs w, int64_t nt64, int64_t n2,
+                                                         int64_t T, int64_t HD, float *mu_slot,
+                                                         float *mu_g, float *mu_s) {
     __shared__ double bs[32][kFinCh];
     __shared__ float rx[4][kFinCh];
     __shared__ float rn[4][kFinCh];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t ch = (int64_t)blockIdx.x * kFinCh + lane;
+    const int lane = threadIdx.x, c = lane & (kFinCh - 1), q = lane >> 4;
+    const int64_t ch = (int64_t)blockIdx.x * kFinCh + c;
     const int nb = n2 >= 32 ? (int)(n2 / 32) : 1;  // blocks of 32 nodes (<= 32)
     float kx = -__builtin_huge_valf(), kn = __builtin_huge_valf();
     const int64_t chc = ch < HD ? ch : HD - 1;
-    for (int b = wave; b < nb; b += 4) {
+    for (int b = q; b < nb; b += 4) {
         double v[32];
         float xv[32], nv[32];
 #pragma unroll
@@ -219,24 +296,23 @@ __global__ __launch_bounds__(256) void kv_finalize_kernel(KvWs w, int64_t nt64, 
             kx = ok ? fmaxf(kx, xv[i]) : kx;
             kn = ok ? fminf(kn, nv[i]) : kn;
         }
-        bs[b][lane] = tree32(v);
+        bs[b][c] = tree32(v);
     }
-    rx[wave][lane] = kx;
-    rn[wave][lane] = kn;
+    rx[q][c] = kx;
+    rn[q][c] = kn;
     __syncthreads();
-    if (wave != 0) return;
     float amax = 0.0f;
-    if (ch < HD) {
+    if (q == 0 && ch < HD) {
         double v[32];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) v[i] = (i < nb) ? bs[i][lane] : 0.0;
+        for (int i = 0; i < 32; ++i) v[i] = (i < nb) ? bs[i][c] : 0.0;
         const double S = tree32(v);
         const float mu = (float)(S / (double)T);
         mu_slot[ch] = mu;
         if (mu_g) mu_g[ch] = mu;
         if (mu_s) mu_s[ch] = mu;
-        const float x = fmaxf(fmaxf(rx[0][lane], rx[1][lane]), fmaxf(rx[2][lane], rx[3][lane]));
-        const float n = fminf(fminf(rn[0][lane], rn[1][lane]), fminf(rn[2][lane], rn[3][lane]));
+        const float x = fmaxf(fmaxf(rx[0][c], rx[1][c]), fmaxf(rx[2][c], rx[3][c]));
+        const float n = fminf(fminf(rn[0][c], rn[1][c]), fminf(rn[2][c], rn[3][c]));
         amax = fmaxf(x - mu, mu - n);
     }
     amax = wave_max(amax);
@@ -244,12 +320,16 @@ __global__ __launch_bounds__(256) void kv_finalize_kernel(KvWs w, int64_t nt64, 
 }
 
 // One lane per 1x16 block along the (head, dim) axis; blockIdx.y = 0: keys
-// (K_s = RN(K - mu)), 1: values.  The prologue reduces the key / value amax
-// partials, derives both tensor scales (workgroup (0,0) stores the decode
-// scales into the slot and the sink copies) and builds the (S, r) table of
-// the workgroup's tensor.  Blocks below the sink length are also written to
-// the sink copies.
-template <bool FOUR_OVER_SIX>
+// (K_s = RN(K - mu)), 1: values.  The first two blocks of each lane are
+// loaded before the prologue, which reduces the key / value amax partials,
+// derives both tensor scales (workgroup (0,0) stores the decode scales into
+// the slot and the sink copies) and builds the (S, r) table of the
+// workgroup's tensor; afterwards each lane keeps two blocks in flight.  When
+// the grid stride is a multiple of the blocks per token (MU_FIXED) every
+// block of a lane starts at the same channel, and the lane holds its 16 key
+// means in registers; otherwise they are re-read per block.  Blocks below
+// the sink length are also written to the sink copies.
+template <bool FOUR_OVER_SIX, bool MU_FIXED>
 __global__ __launch_bounds__(256) void kv_encode_kernel(
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, int64_t nblk, int64_t HD,
     const float *__restrict__ kpart, int nk, const float *__restrict__ vpart, int nv,
@@ -258,6 +338,21 @@ __global__ __launch_bounds__(256) void kv_encode_kernel(
     __shared__ float red[2][4];
     __shared__ float sh[4];
     const int which = blockIdx.y;  // 0: keys, 1: values
+    const uint16_t *x = which ? V : K;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    Raw16Bf16 r0, r1;
+    if (b < nblk) load_raw16(x + b * 16, r0);
+    if (b + stride < nblk) load_raw16(x + (b + stride) * 16, r1);
+    // channel of the block's first element, advanced without division: (16 b) mod HD
+    int64_t ch0 = (b * 16) % HD;
+    const int64_t step = (stride * 16) % HD;
+    float mu[16];
+    if (MU_FIXED && which == 0 && b < nblk) {
+        Raw16F32 m;
+        load_raw16(slot.mu + ch0, m);
+        unpack16(m, mu);
+    }
     float ak = 0.0f, av = 0.0f;
     for (int i = threadIdx.x; i < nk; i += blockDim.x) ak = fmaxf(ak, kpart[i]);
     for (int i = threadIdx.x; i < nv; i += blockDim.x) av = fmaxf(av, vpart[i]);
@@ -296,31 +391,27 @@ __global__ __launch_bounds__(256) void kv_encode_kernel(
     const float s_dec = sh[2 * which + 1];
     for (int c = threadIdx.x; c < 128; c += blockDim.x) lut[c] = scale_entry((uint32_t)c, s_dec);
     __syncthreads();
-    const uint16_t *x = which ? V : K;
     uint2 *codes = (uint2 *)(which ? slot.vc : slot.kc);
     uint8_t *scales = which ? slot.vs : slot.ks;
     uint2 *gcodes = (uint2 *)(which ? gsink.vc : gsink.kc);
     uint8_t *gscales = which ? gsink.vs : gsink.ks;
     uint2 *scodes = (uint2 *)(which ? ssink.vc : ssink.kc);
     uint8_t *sscales = which ? ssink.vs : ssink.ks;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    // channel of the block's first element, advanced without division: (16 b) mod HD
-    int64_t ch0 = (b * 16) % HD;
-    const int64_t step = (stride * 16) % HD;
-    Raw16Bf16 rn;
-    if (b < nblk) load_raw16(x + b * 16, rn);
     for (; b < nblk; b += stride) {
-        // the next block's load is issued before this block is encoded
-        const Raw16Bf16 r = rn;
-        if (b + stride < nblk) load_raw16(x + (b + stride) * 16, rn);
+        // two blocks ahead are in flight while this one is encoded
+        const Raw16Bf16 r = r0;
+        r0 = r1;
+        if (b + 2 * stride < nblk) load_raw16(x + (b + 2 * stride) * 16, r1);
         float v[16];
         unpack16(r, v);
         if (which == 0) {
-            Raw16F32 m;
-            load_raw16(slot.mu + ch0, m);
-            float mu[16];
-            unpack16(m, mu);
+            if (!MU_FIXED) {
+                Raw16F32 m;
+                load_raw16(slot.mu + ch0, m);
+                unpack16(m, mu);
+                ch0 += step;
+                if (ch0 >= HD) ch0 -= HD;
+            }
 #pragma unroll
             for (int i = 0; i < 16; ++i) v[i] = v[i] - mu[i];
         }
@@ -336,38 +427,61 @@ __global__ __launch_bounds__(256) void kv_encode_kernel(
             scodes[b] = make_uint2(lo, hi);
             sscales[b] = (uint8_t)sc;
         }
-        ch0 += step;
-        if (ch0 >= HD) ch0 -= HD;
     }
 }
 
 hipError_t launch_kv_store(const KvStoreArgs &a, hipStream_t s) {
     const KvDims d = kv_dims(a.T, a.HD);
     KvWs w = carve_ws(a.ws, a.T, a.HD);
-    NVFP4_LAUNCH("kv_stats", kv_stats_kernel, dim3((unsigned)d.nt64, (unsigned)d.gy, 2),
-                 dim3(256), 0, s, a.K, a.V, a.T, a.HD, w);
+    NVFP4_LAUNCH("kv_stats", kv_stats_kernel, dim3((unsigned)(d.nt64 * d.gy), 2), dim3(128), 0,
+                 s, a.K, a.V, a.T, a.HD, d.gy, w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    NVFP4_LAUNCH("kv_finalize", kv_finalize_kernel, dim3((unsigned)d.nfin), dim3(256), 0, s, w,
+    NVFP4_LAUNCH("kv_finalize", kv_finalize_kernel, dim3((unsigned)d.nfin), dim3(64), 0, s, w,
                  d.nt64, d.n2, a.T, a.HD, a.slot.mu,
                  a.g_tokens > 0 ? a.gsink.mu : (float *)nullptr,
                  a.s_tokens > 0 ? a.ssink.mu : (float *)nullptr);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nblk = a.T * a.HD / 16;
+    // Grid: up to kEncodeGrid workgroups per tensor.  If a multiple of
+    // m = NB / gcd(NB, 256) fits (NB = blocks per token), the grid is that
+    // multiple, so the stride in blocks is a multiple of NB.
     int64_t g = (nblk + 255) / 256;
-    if (g > 512) g = 512;
+    if (g > kEncodeGrid) g = kEncodeGrid;
     if (g < 1) g = 1;
+    const int64_t NB = a.HD / 16;
+    int64_t gc = NB, tw = 256;
+    while (tw > 1 && gc % 2 == 0) {
+        gc /= 2;
+        tw /= 2;
+    }
+    bool fixed = false;
+    if (gc <= g) {
+        g = (g / gc) * gc;
+        fixed = true;
+    } else if (gc <= 2 * kEncodeGrid) {
+        g = gc;
+        fixed = true;
+    }
     const int64_t g_blk = a.g_tokens * a.HD / 16, s_blk = a.s_tokens * a.HD / 16;
     const int nk = (int)d.nfin, nv = (int)(d.nt64 * d.gy);
-    if (a.search == 1)
-        NVFP4_LAUNCH("kv_encode", kv_encode_kernel<true>, dim3((unsigned)g, 2), dim3(256), 0, s,
-                     a.K, a.V, nblk, a.HD, (const float *)w.kpart, nk, (const float *)w.vpart, nv,
-                     a.slot, a.gsink, a.ssink, g_blk, s_blk);
-    else
-        NVFP4_LAUNCH("kv_encode", kv_encode_kernel<false>, dim3((unsigned)g, 2), dim3(256), 0, s,
-                     a.K, a.V, nblk, a.HD, (const float *)w.kpart, nk, (const float *)w.vpart, nv,
-                     a.slot, a.gsink, a.ssink, g_blk, s_blk);
+#define NVFP4_ENC(F46, FIX)                                                                   \
+    NVFP4_LAUNCH("kv_encode", (kv_encode_kernel<F46, FIX>), dim3((unsigned)g, 2), dim3(256), 0, \
+                 s, a.K, a.V, nblk, a.HD, (const float *)w.kpart, nk, (const float *)w.vpart, nv, \
+                 a.slot, a.gsink, a.ssink, g_blk, s_blk)
+    if (a.search == 1) {
+        if (fixed)
+            NVFP4_ENC(true, true);
+        else
+            NVFP4_ENC(true, false);
+    } else {
+        if (fixed)
+            NVFP4_ENC(false, true);
+        else
+            NVFP4_ENC(false, false);
+    }
+#undef NVFP4_ENC
     return hipGetLastError();
 }
 
