@@ -6,36 +6,82 @@
 // tensor-wise FP32 scale on each ("NVFP4 training").
 //
 // gfx950 has no MFMA that takes an E4M3 scale per 16 elements (its scaled
-// FP4 MFMA takes power-of-two E8M0 scales per 32), so each NVFP4 tile is
+// FP4 MFMA takes power-of-two E8M0 scales per 32), so each NVFP4 operand is
 // expanded exactly and fed to the fp16 MFMA (same dense rate as bf16):
-//   A_hat = V(code) * sigma,  sigma = 2^E * F  (E4M3: F = 1 + m/8, or m for a
-//   subnormal with E = -9).  v_cvt_scalef32_pk_f16_fp4 gives V * 2^E exactly,
-//   one packed fp16 multiply by F gives V * sigma exactly (at most 6
-//   significant bits, magnitude in [2^-10, 2688]: exact in fp16, as in bf16).
+//   A_hat = V(code) * sigma,  sigma the E4M3 block scale.
+//   v_cvt_scalef32_pk_f16_fp4 gives V exactly, one packed fp16 multiply by
+//   sigma gives V * sigma exactly (at most 6 significant bits, magnitude in
+//   [2^-10, 2688]: exact in fp16).
 // The FP32 tensor scales are applied once in the epilogue:
 //   Y = RN(RN(s_A * s_W) * acc), acc the fp32 MFMA accumulation.
 //
-// Tiling: workgroup 256 threads = 4 waves (2 x 2), output tile BM x BN =
-// 256 x 256, K step 64.  Each wave owns a 128 x 128 sub-tile = 4 x 4 blocks
-// of v_mfma_f32_32x32x16_f16 (256 fp32 accumulators per lane).  Every packed
-// tile is expanded once per workgroup into LDS as fp16 (row stride 72 halfs:
-// the 16-byte fragment reads of 16 consecutive rows hit disjoint banks), two
-// LDS stages: while the MFMAs consume stage k, the packed tile k+1 (already in
-// registers) is expanded into the other stage and tile k+2 is fetched.
+// Operand layout in the MFMA: the 32x32x16 MFMA pairs lane l's 8 K values
+// of row (l & 31) with the same 8 K positions of the other operand, and the
+// contraction does not care which K positions those are, so lane half
+// h = l >> 5 takes the contiguous K range [128 h, 128 h + 128) of each
+// 256-deep K step (16 consecutive code dwords = 64 bytes, and the 8 scale
+// bytes of those blocks); MFMA substep s uses dword s of both halves.  The
+// same assignment on both operands keeps the product exact.
+//
+// Tiling: workgroup 4 waves (2 x 2), tile BM x BN = 256 x 192; each wave owns
+// 128 x 96 = 4 x 3 blocks of v_mfma_f32_32x32x16_f16 (192 fp32 accumulators
+// per lane).  Workgroups are mapped to tiles XCD by XCD: XCD x takes the x-th
+// contiguous (row-major) range of tiles, so tiles that share operand rows
+// share an L2.
+//
+// Data flow (K % 256 == 0): the packed tiles of a K step (codes 128 bytes
+// per row, scales 16 bytes per row or 16-row group) go from memory straight
+// to LDS (global_load_lds, 16 bytes per lane, 8 lanes per 128-byte row, so
+// every load instruction covers 8 whole cache lines), two LDS stages.  The
+// 16-byte columns of each 8-row block are XOR-swizzled by the row (column c
+// of row r sits in slot c ^ (r & 7)), so the fragment reads -- 8 rows per
+// column -- hit 8 different bank groups.  Per K step: barrier; each wave
+// reads its whole step of fragments from LDS into registers; the loads of
+// the next step are issued into the other stage; the 16 MFMA substeps run
+// from registers, expanding each fragment dword just before its MFMAs.
+// Other K: the same MFMA schedule from per-lane loads straight from memory,
+// with blocks past K read as zero.
+#include <utility>
+
 #include "device.hpp"
 #include "launch.hpp"
 
 namespace nvfp4 {
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int LDS_STRIDE = BK + 8;  // halfs per row
-constexpr int WM = BM / 2, WN = BN / 2;
-constexpr int FM = WM / 32, FN = WN / 32;  // MFMA blocks per wave
+constexpr int FM = 4, FN = 3;               // MFMA blocks per wave
+constexpr int WM = 32 * FM, WN = 32 * FN;   // 128 x 96 per wave
+constexpr int BM = 2 * WM, BN = 2 * WN;     // 256 x 192 per workgroup
+constexpr int BK = 256;                     // K per step
+constexpr int NSUB = BK / 16;               // MFMA substeps per step
+constexpr int kXcds = 8;
 
-// Expand 8 codes (one dword) to 8 fp16 values V * sigma: the hardware
-// converter gives V exactly in fp16 (scale 1), one packed multiply by the
-// block scale sigma (exact in fp16: E4M3 values lie in [2^-9, 448]) gives
-// V * sigma exactly.
+// LDS stage layout (bytes): A codes (BM / 8 blocks of 8 rows x 128 bytes),
+// W codes, A scales (16 bytes per row), W scales (16 bytes per 16-row group).
+constexpr int kAOff = 0;
+constexpr int kBOff = kAOff + BM * 128;
+constexpr int kASOff = kBOff + BN * 128;
+constexpr int kBSOff = kASOff + BM * 16;
+constexpr int kStage = kBSOff + (BN / 16) * 16 + 64;  // 61696 bytes
+constexpr int kLdsBytes = 2 * kStage;
+static_assert(kStage % 256 == 0, "stage alignment");
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void *lvoid;  // LDS
+
+struct GemmArgs {
+    const uint8_t *a_codes, *a_scales, *w_codes, *w_scales;
+    int64_t M, N, K;
+};
+
+// One lane's share of one operand fragment (32 rows x 256 K) for one K
+// step: 16 code dwords (4 chunks of 16 bytes) and 8 scale bytes.
+struct Frag {
+    u32x4 q[4];
+    u32x2 sc;
+};
+
+// Eight fp16 values V * sigma from one code dword (8 codes, element 2j in
+// the low nibble of byte j).
 __device__ __forceinline__ f16x8 expand8(uint32_t w, f16x2 sig) {
     f16x8 o;
     f16x2 t;
@@ -46,97 +92,200 @@ __device__ __forceinline__ f16x8 expand8(uint32_t w, f16x2 sig) {
     return o;
 }
 
-// One thread's share of staging one K step: for each of 4 "parts" (A rows
-// lrow and lrow + 128, W rows lrow and lrow + 128), 32 consecutive K elements
-// = 2 blocks = 16 code bytes + 2 scale bytes.
-struct Part {
-    u32x4 q;
-    uint32_t sc;  // two E4M3 scale bytes in the low 16 bits
-};
-
-struct GemmArgs {
-    const uint8_t *a_codes, *a_scales, *w_codes, *w_scales;
-    int64_t M, N, K;
-};
-
-// Per-thread source pointers of the 4 parts at K step 0 (rows clamped into
-// range; edge tiles mask them later).
-struct PartPtrs {
-    const uint8_t *c[4];
-    const uint8_t *s[4];
-    uint32_t rowmask[4];  // ~0 if the part's row exists, else 0
-};
-
-__device__ __forceinline__ void part_ptrs(PartPtrs &pp, const GemmArgs &g, int64_t m0, int64_t n0,
-                                          int tid) {
-    const int64_t KB = g.K >> 4, kbytes = g.K >> 1;
-    const int lrow = tid >> 1, kseg = (tid & 1) * 32;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const bool isA = p < 2;
-        const int64_t rows = isA ? g.M : g.N;
-        const int64_t r = (isA ? m0 : n0) + lrow + (p & 1) * 128;
-        const int64_t rc = r < rows ? r : rows - 1;
-        const int64_t srow = isA ? rc : (rc >> 4);
-        pp.c[p] = (isA ? g.a_codes : g.w_codes) + rc * kbytes + kseg / 2;
-        pp.s[p] = (isA ? g.a_scales : g.w_scales) + srow * KB + kseg / 16;
-        pp.rowmask[p] = r < rows ? ~0u : 0u;
-    }
-}
-
-// Fetch part P of K step kt.  Fast path (EDGE = false): the whole tile lies
-// inside the matrices and K % 64 == 0.  Edge path: clamped, in-bounds loads,
-// codes of missing rows or blocks zeroed (code 0 is +0 whatever the scale).
-template <int P, bool EDGE>
-__device__ __forceinline__ void fetch_part(Part &pt, const PartPtrs &pp, const GemmArgs &g,
-                                           int64_t kt, int tid) {
-    if (!EDGE) {
-        pt.q = *(const u32x4 *)(pp.c[P] + kt * (BK / 2));
-        pt.sc = *(const uint16_t *)(pp.s[P] + kt * (BK / 16));
-        return;
-    }
-    const int64_t KB = g.K >> 4;
-    const int64_t kb0 = kt * (BK / 16) + (tid & 1) * 2;  // first of the two blocks
-    const bool b0 = kb0 < KB, b1 = kb0 + 1 < KB;
-    // base pointers address block (tid & 1) * 2 of K step 0
-    const int64_t kbc = b1 ? kb0 : (KB >= 2 ? KB - 2 : 0);
-    const int64_t dblk = kbc - (tid & 1) * 2;  // blocks from the base pointer
-    u32x4 q;
-    uint32_t sc;
-    if (KB >= 2) {
-        q = *(const u32x4 *)(pp.c[P] + dblk * 8);
-        sc = (uint32_t)pp.s[P][dblk] | ((uint32_t)pp.s[P][dblk + 1] << 8);
-    } else {
-        const uint2 q2 = *(const uint2 *)(pp.c[P] + dblk * 8);
-        q = u32x4{q2.x, q2.y, 0u, 0u};
-        sc = pp.s[P][dblk];
-    }
-    const bool up = KB >= 2 && !b1;  // only the last block is valid: it is in the upper half
-    const uint32_t m0k = b0 ? pp.rowmask[P] : 0u, m1k = b1 ? pp.rowmask[P] : 0u;
-    pt.q = u32x4{(up ? q.z : q.x) & m0k, (up ? q.w : q.y) & m0k, q.z & m1k, q.w & m1k};
-    pt.sc = up ? (sc >> 8) : sc;
-}
-
+// Block scales (E4M3) of blocks 2p and 2p + 1 of a fragment's step, as fp16
+// (exact: every E4M3 value is an fp16 value).
 template <int P>
-__device__ __forceinline__ void expand_part(const Part &pt, _Float16 *stage, int tid) {
-    const int lrow = tid >> 1, kseg = (tid & 1) * 32;
-    _Float16 *d = stage + ((P >= 2 ? BM : 0) + lrow + (P & 1) * 128) * LDS_STRIDE + kseg;
-    const f16x2 sg = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pt.sc, 1.0f, false);
-    const f16x2 s0 = f16x2{sg.x, sg.x}, s1 = f16x2{sg.y, sg.y};
-    *(f16x8 *)(d) = expand8(pt.q.x, s0);
-    *(f16x8 *)(d + 8) = expand8(pt.q.y, s0);
-    *(f16x8 *)(d + 16) = expand8(pt.q.z, s1);
-    *(f16x8 *)(d + 24) = expand8(pt.q.w, s1);
+__device__ __forceinline__ f16x2 sigma_pair(const u32x2 &sc) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(P < 2 ? sc.x : sc.y, 1.0f, (P & 1) != 0);
 }
 
-template <bool OUT_BF16, bool EDGE>
-__device__ __forceinline__ void gemm_tile(const GemmArgs &g, const float *__restrict__ a_sdec,
-                                          const float *__restrict__ w_sdec, void *__restrict__ yv,
-                                          _Float16 *lds, int64_t m0, int64_t n0) {
-    auto stage = [&](int s) { return lds + s * (BM + BN) * LDS_STRIDE; };
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+__device__ __forceinline__ uint32_t dword_of(const u32x4 &q, int i) {
+    return i == 0 ? q.x : i == 1 ? q.y : i == 2 ? q.z : q.w;
+}
+
+// Row pointers of one lane's fragment (row clamped into range: rows past
+// the end compute values that are never stored).
+struct FragPtr {
+    const uint8_t *c;  // codes of the row, + 64 h bytes
+    const uint8_t *s;  // scales of the row (2-D: of its 16-row group), + 8 h
+};
+
+__device__ __forceinline__ FragPtr frag_ptr(const uint8_t *codes, const uint8_t *scales,
+                                            int64_t row, int64_t rows, int64_t K, bool two_d,
+                                            int h) {
+    const int64_t r = row < rows ? row : rows - 1;
+    const int64_t KB = K >> 4;
+    FragPtr p;
+    p.c = codes + r * (K >> 1) + h * 64;
+    p.s = scales + (two_d ? (r >> 4) : r) * KB + h * 8;
+    return p;
+}
+
+// General path (any K % 16 == 0): blocks at or past K / 16 read as code 0
+// and scale 0 (+0 whatever the other operand); loads are 8-byte (codes) and
+// 1-byte (scales) and stay inside the row.
+__device__ __forceinline__ void load_frag_general(Frag &f, const FragPtr &p, int64_t kt,
+                                                  int64_t K, int h) {
+    const int64_t KB = K >> 4;
+    const int64_t kb0 = kt * (BK / 16) + h * 8;  // first block of this lane's half
+    const uint8_t *crow = p.c - h * 64, *srow = p.s - h * 8;
+    uint32_t d[16], sb[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        const bool ok = kb0 + b < KB;
+        const int64_t kb = ok ? kb0 + b : 0;
+        const uint2 v = *(const uint2 *)(crow + kb * 8);
+        d[2 * b] = ok ? v.x : 0u;
+        d[2 * b + 1] = ok ? v.y : 0u;
+        sb[b] = ok ? (uint32_t)srow[kb] : 0u;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) f.q[c] = u32x4{d[4 * c], d[4 * c + 1], d[4 * c + 2], d[4 * c + 3]};
+    f.sc = u32x2{sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24),
+                 sb[4] | (sb[5] << 8) | (sb[6] << 16) | (sb[7] << 24)};
+}
+
+// MFMA substep s (K positions 8 s .. 8 s + 7 of each lane half) over the
+// wave's 4 x 3 blocks: block s / 2 of the half, scale byte s / 2.
+template <int S>
+__device__ __forceinline__ void substep(f32x16 (&acc)[FM][FN], const Frag (&A)[FM],
+                                        const Frag (&B)[FN]) {
+    constexpr int c = S >> 2, i4 = S & 3, hi = (S >> 1) & 1;
+    f16x8 a[FM], b[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const f16x2 sg = sigma_pair<c>(A[i].sc);
+        const _Float16 g = hi ? sg.y : sg.x;
+        a[i] = expand8(dword_of(A[i].q[c], i4), f16x2{g, g});
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const f16x2 sg = sigma_pair<c>(B[j].sc);
+        const _Float16 g = hi ? sg.y : sg.x;
+        b[j] = expand8(dword_of(B[j].q[c], i4), f16x2{g, g});
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+}
+
+// Buffer descriptors over the four packed arrays and this lane's byte
+// offsets into them for its share of every step's direct-to-LDS loads:
+// A code blocks 8w .. 8w + 7 and W code blocks 6w .. 6w + 5 of the tile
+// (8 rows each; lane j loads 16-byte column (j & 7) ^ (j >> 3) of row
+// j >> 3 into slot j), the A scales of tile rows 64w + j, and (wave 0, lanes
+// below 12) the W scales of the tile's 16-row groups.  Rows past the matrix
+// edge are clamped to the last row.  The step's offset is a scalar added at
+// each load.  (The host sends matrices of 2^31 bytes or more to the general
+// path, so every offset fits.)
+struct StageSrc {
+    __amdgpu_buffer_rsrc_t ac, wc, as, ws;
+    uint32_t a[BM / 32], w[BN / 32], asr, wsr;
+};
+
+__device__ __forceinline__ void stage_src(StageSrc &q, const GemmArgs &g, int64_t m0, int64_t n0,
+                                          int wave, int lane) {
+    const int64_t kbytes = g.K >> 1, KB = g.K >> 4;
+    q.ac = __builtin_amdgcn_make_buffer_rsrc((void *)g.a_codes, (short)0, (int)(g.M * kbytes),
+                                             kBufferWord3);
+    q.wc = __builtin_amdgcn_make_buffer_rsrc((void *)g.w_codes, (short)0, (int)(g.N * kbytes),
+                                             kBufferWord3);
+    q.as = __builtin_amdgcn_make_buffer_rsrc((void *)g.a_scales, (short)0, (int)(g.M * KB),
+                                             kBufferWord3);
+    q.ws = __builtin_amdgcn_make_buffer_rsrc((void *)g.w_scales, (short)0,
+                                             (int)((g.N >> 4) * KB), kBufferWord3);
+    const int rib = lane >> 3, gcol = (lane & 7) ^ rib;
+#pragma unroll
+    for (int bb = 0; bb < BM / 32; ++bb) {
+        const int64_t row0 = m0 + (wave * (BM / 32) + bb) * 8 + rib;
+        const int64_t row = row0 < g.M ? row0 : g.M - 1;
+        q.a[bb] = (uint32_t)(row * kbytes) + gcol * 16;
+    }
+#pragma unroll
+    for (int bb = 0; bb < BN / 32; ++bb) {
+        const int64_t row0 = n0 + (wave * (BN / 32) + bb) * 8 + rib;
+        const int64_t row = row0 < g.N ? row0 : g.N - 1;
+        q.w[bb] = (uint32_t)(row * kbytes) + gcol * 16;
+    }
+    const int64_t ar0 = m0 + wave * 64 + lane;
+    q.asr = (uint32_t)((ar0 < g.M ? ar0 : g.M - 1) * KB);
+    const int64_t gr0 = (n0 >> 4) + lane, glast = (g.N >> 4) - 1;
+    q.wsr = (uint32_t)((gr0 < glast ? gr0 : glast) * KB);
+}
+
+// Issue this wave's direct-to-LDS loads of K step kt into `stage`.
+__device__ __forceinline__ void stage_load(const StageSrc &q, uint8_t *stage, int64_t kt, int wave,
+                                           int lane) {
+    const uint32_t kc = (uint32_t)kt * 128, ks = (uint32_t)kt * 16;
+#pragma unroll
+    for (int bb = 0; bb < BM / 32; ++bb)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            q.ac, (lvoid)(stage + kAOff + (wave * (BM / 32) + bb) * 1024), 16, q.a[bb], kc, 0, 0);
+#pragma unroll
+    for (int bb = 0; bb < BN / 32; ++bb)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            q.wc, (lvoid)(stage + kBOff + (wave * (BN / 32) + bb) * 1024), 16, q.w[bb], kc, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(q.as, (lvoid)(stage + kASOff + wave * 1024), 16,
+                                             q.asr, ks, 0, 0);
+    if (wave == 0 && lane < BN / 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(q.ws, (lvoid)(stage + kBSOff), 16, q.wsr, ks, 0,
+                                                 0);
+}
+
+// The wave's fragments of one K step from LDS: lane (r, h) reads, for each
+// fragment row R, the 16-byte columns 4h .. 4h + 3 (un-swizzled) and the 8
+// scale bytes of its half.
+__device__ __forceinline__ void stage_read(Frag (&A)[FM], Frag (&B)[FN], const uint8_t *stage,
+                                           int wm, int wn, int r, int h) {
+    const int rib = r & 7;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+        A[i].sc = *(const u32x2 *)(stage + kASOff + (wm * WM + i * 32 + r) * 16 + h * 8);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+        B[j].sc = *(const u32x2 *)(stage + kBSOff + ((wn * WN + j * 32 + r) >> 4) * 16 + h * 8);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int slot = ((h * 4 + c) ^ rib) * 16 + rib * 128;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            A[i].q[c] = *(const u32x4 *)(stage + kAOff + ((wm * WM + i * 32 + r) >> 3) * 1024 + slot);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            B[j].q[c] = *(const u32x4 *)(stage + kBOff + ((wn * WN + j * 32 + r) >> 3) * 1024 + slot);
+    }
+}
+
+template <int... S>
+__device__ __forceinline__ void step_all(f32x16 (&acc)[FM][FN], const Frag (&A)[FM],
+                                         const Frag (&B)[FN], std::integer_sequence<int, S...>) {
+    (substep<S>(acc, A, B), ...);
+}
+
+template <bool OUT_BF16, bool KFAST>
+__global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float *__restrict__ a_sdec,
+                                                        const float *__restrict__ w_sdec,
+                                                        void *__restrict__ yv) {
     const int64_t M = g.M, N = g.N, K = g.K;
+    const int64_t tn_count = (N + BN - 1) / BN;
+    const int64_t ntiles = ((M + BM - 1) / BM) * tn_count;
+    // XCD-aware tile order: workgroup b runs on XCD b % 8; XCD x takes the
+    // x-th contiguous range of tiles (tiles past 8 * floor(n / 8) map to
+    // themselves).
+    const int64_t b = blockIdx.x;
+    const int64_t per = ntiles / kXcds;
+    const int64_t t = b < per * kXcds ? (b % kXcds) * per + b / kXcds : b;
+    const int64_t m0 = (t / tn_count) * BM, n0 = (t % tn_count) * BN;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = lane >> 5, r = lane & 31, wm = wave >> 1, wn = wave & 1;
+    const int64_t mw = m0 + wm * WM, nw = n0 + wn * WN;
+    // a wave whose sub-tile lies wholly past the matrix edge computes nothing
+    // (it still takes its share of the loads and every barrier)
+    const bool active = mw < M && nw < N;
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -144,88 +293,69 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const float *__rest
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
     const int64_t nk = (K + BK - 1) / BK;
-    PartPtrs pp;
-    part_ptrs(pp, g, m0, n0, tid);
-    Part p0, p1, p2, p3;
-    fetch_part<0, EDGE>(p0, pp, g, 0, tid);
-    fetch_part<1, EDGE>(p1, pp, g, 0, tid);
-    fetch_part<2, EDGE>(p2, pp, g, 0, tid);
-    fetch_part<3, EDGE>(p3, pp, g, 0, tid);
-    expand_part<0>(p0, stage(0), tid);
-    expand_part<1>(p1, stage(0), tid);
-    expand_part<2>(p2, stage(0), tid);
-    expand_part<3>(p3, stage(0), tid);
-    // the fast path never reads past the last K step
-    const int64_t last = EDGE ? (int64_t)1 << 40 : nk - 1;
-    fetch_part<0, EDGE>(p0, pp, g, 1 < last ? 1 : last, tid);
-    fetch_part<1, EDGE>(p1, pp, g, 1 < last ? 1 : last, tid);
-    fetch_part<2, EDGE>(p2, pp, g, 1 < last ? 1 : last, tid);
-    fetch_part<3, EDGE>(p3, pp, g, 1 < last ? 1 : last, tid);
-    __syncthreads();
-
-    const int frow = lane & 31, fk = (lane >> 5) * 8;
-    const int aoff = (wm * WM + frow) * LDS_STRIDE + fk;
-    const int woff = (BM + wn * WN + frow) * LDS_STRIDE + fk;
-    f16x8 fa[2][FM], fb[2][FN];
-    {
-        const _Float16 *S = stage(0);
-#pragma unroll
-        for (int i = 0; i < FM; ++i) fa[0][i] = *(const f16x8 *)(S + aoff + i * 32 * LDS_STRIDE);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) fb[0][j] = *(const f16x8 *)(S + woff + j * 32 * LDS_STRIDE);
-    }
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const _Float16 *S = stage(cur);
-        _Float16 *Nx = stage(cur ^ 1);
-        // K step fetched this iteration (past the end: clamped on the fast
-        // path, zeroed on the edge path; either way never used)
-        const int64_t kf = (kt + 2 < last) ? kt + 2 : last;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int c = kk & 1;
-            if (kk < 3) {
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-                    fa[c ^ 1][i] = *(const f16x8 *)(S + aoff + i * 32 * LDS_STRIDE + (kk + 1) * 16);
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    fb[c ^ 1][j] = *(const f16x8 *)(S + woff + j * 32 * LDS_STRIDE + (kk + 1) * 16);
+    Frag A[FM], B[FN];
+    if (KFAST) {
+        extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+        StageSrc src;
+        stage_src(src, g, m0, n0, wave, lane);
+        stage_load(src, lds, 0, wave, lane);
+        // Each iteration: this wave's loads of step kt have landed; after the
+        // barrier so have everyone's, and nobody still reads the stage that
+        // the loads of step kt + 1 overwrite.  The last iteration reloads its
+        // own step into the idle stage (never read), keeping the loop free of
+        // branches.  Both loops take the same barriers.
+        if (active) {
+            for (int64_t kt = 0; kt < nk; ++kt) {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                __syncthreads();
+                const int64_t kn = kt + 1 < nk ? kt + 1 : kt;
+                stage_read(A, B, lds + (kt & 1) * kStage, wm, wn, r, h);
+                stage_load(src, lds + ((kt + 1) & 1) * kStage, kn, wave, lane);
+                step_all(acc, A, B, std::make_integer_sequence<int, NSUB>{});
             }
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[c][i], fb[c][j],
-                                                                       acc[i][j], 0, 0, 0);
-            // stage the next K step (harmless past the end of K)
-            if (kk == 0) { expand_part<0>(p0, Nx, tid); fetch_part<0, EDGE>(p0, pp, g, kf, tid); }
-            if (kk == 1) { expand_part<1>(p1, Nx, tid); fetch_part<1, EDGE>(p1, pp, g, kf, tid); }
-            if (kk == 2) { expand_part<2>(p2, Nx, tid); fetch_part<2, EDGE>(p2, pp, g, kf, tid); }
-            if (kk == 3) { expand_part<3>(p3, Nx, tid); fetch_part<3, EDGE>(p3, pp, g, kf, tid); }
+        } else {
+            for (int64_t kt = 0; kt < nk; ++kt) {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                __syncthreads();
+                const int64_t kn = kt + 1 < nk ? kt + 1 : kt;
+                stage_load(src, lds + ((kt + 1) & 1) * kStage, kn, wave, lane);
+            }
         }
-        __syncthreads();
+        // no load into LDS is still in flight when the wave leaves
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else if (active) {
+        FragPtr pa[FM], pb[FN];
 #pragma unroll
-        for (int i = 0; i < FM; ++i) fa[0][i] = *(const f16x8 *)(Nx + aoff + i * 32 * LDS_STRIDE);
+        for (int i = 0; i < FM; ++i)
+            pa[i] = frag_ptr(g.a_codes, g.a_scales, mw + i * 32 + r, M, K, false, h);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) fb[0][j] = *(const f16x8 *)(Nx + woff + j * 32 * LDS_STRIDE);
+        for (int j = 0; j < FN; ++j)
+            pb[j] = frag_ptr(g.w_codes, g.w_scales, nw + j * 32 + r, N, K, true, h);
+        for (int64_t kt = 0; kt < nk; ++kt) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) load_frag_general(A[i], pa[i], kt, K, h);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) load_frag_general(B[j], pb[j], kt, K, h);
+            step_all(acc, A, B, std::make_integer_sequence<int, NSUB>{});
+        }
     }
+    if (!active) return;
 
     const float scale = (*a_sdec) * (*w_sdec);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            const int64_t col = n0 + wn * WN + j * 32 + (lane & 31);
-            const int64_t rbase = m0 + wm * WM + i * 32 + (lane >> 5) * 4;
+            const int64_t col = nw + j * 32 + r;
+            const int64_t rbase = mw + i * 32 + h * 4;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t row = rbase + (r >> 2) * 8 + (r & 3);
-                const float v = scale * acc[i][j][r];
-                if (!EDGE || (row < M && col < N)) {
+            for (int e = 0; e < 16; ++e) {
+                const int64_t row = rbase + (e >> 2) * 8 + (e & 3);
+                const float v = scale * acc[i][j][e];
+                if (row < M && col < N) {
                     if (OUT_BF16)
                         ((__bf16 *)yv)[row * N + col] = (__bf16)v;
                     else
@@ -235,45 +365,43 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const float *__rest
         }
 }
 
-template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float *__restrict__ a_sdec,
-                                                        const float *__restrict__ w_sdec,
-                                                        void *__restrict__ yv) {
-    extern __shared__ __attribute__((aligned(16))) _Float16 lds[];
-    const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
-    const bool interior = (m0 + BM <= g.M) && (n0 + BN <= g.N) && (g.K % BK == 0);
-    if (interior)
-        gemm_tile<OUT_BF16, false>(g, a_sdec, w_sdec, yv, lds, m0, n0);
-    else
-        gemm_tile<OUT_BF16, true>(g, a_sdec, w_sdec, yv, lds, m0, n0);
-}
-
-constexpr size_t kLdsBytes = (size_t)2 * (BM + BN) * LDS_STRIDE * sizeof(_Float16);
-
 hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_sdec,
                             const uint8_t *w_codes, const uint8_t *w_scales,
                             const float *w_sdec, int64_t M, int64_t N, int64_t K, void *y,
                             int ydtype, hipStream_t s) {
     if (M == 0 || N == 0) return hipSuccess;
+    const int64_t ntiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const dim3 grid((unsigned)ntiles);
+    const GemmArgs g{a_codes, a_scales, w_codes, w_scales, M, N, K};
+    // LDS path: K a multiple of the step, and buffer offsets that fit 31 bits
+    const bool fast = K % BK == 0 && M * (K / 2) < ((int64_t)1 << 31) &&
+                      N * (K / 2) < ((int64_t)1 << 31);
     static bool attr_set = false;
     if (!attr_set) {
-        const void *fns[2] = {(const void *)gemm_w4a4_kernel<true>,
-                              (const void *)gemm_w4a4_kernel<false>};
+        const void *fns[2] = {(const void *)gemm_w4a4_kernel<true, true>,
+                              (const void *)gemm_w4a4_kernel<false, true>};
         for (const void *f : fns) {
             hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)kLdsBytes);
+                                               kLdsBytes);
             if (e != hipSuccess) return e;
         }
         attr_set = true;
     }
-    dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
-    GemmArgs g{a_codes, a_scales, w_codes, w_scales, M, N, K};
-    if (ydtype == kBF16)
-        NVFP4_LAUNCH("gemm_w4a4", gemm_w4a4_kernel<true>, grid, dim3(256), kLdsBytes, s, g,
-                     a_sdec, w_sdec, y);
-    else
-        NVFP4_LAUNCH("gemm_w4a4", gemm_w4a4_kernel<false>, grid, dim3(256), kLdsBytes, s, g,
-                     a_sdec, w_sdec, y);
+#define NVFP4_GEMM(BF, KF)                                                                  \
+    NVFP4_LAUNCH("gemm_w4a4", (gemm_w4a4_kernel<BF, KF>), grid, dim3(256), KF ? kLdsBytes : 0, \
+                 s, g, a_sdec, w_sdec, y)
+    if (ydtype == kBF16) {
+        if (fast)
+            NVFP4_GEMM(true, true);
+        else
+            NVFP4_GEMM(true, false);
+    } else {
+        if (fast)
+            NVFP4_GEMM(false, true);
+        else
+            NVFP4_GEMM(false, false);
+    }
+#undef NVFP4_GEMM
     return hipGetLastError();
 }
 
