@@ -213,7 +213,46 @@ def run_gemm_attn(nv, args, dev):
     flops = 2.0 * M * N * K
     kms = kt["gemm_w4a4"][1]
     return {"ms": ms, "wall_ms": wall, "tflops": flops / ms / 1e9, "kernel_ms": kms,
-            "kernel_tflops": flops / kms / 1e9, "flops": flops, "kernels": kt}
+            "kernel_tflops": flops / kms / 1e9, "flops": flops, "kernels": kt,
+            "dense_bf16_tflops": dense_bf16_tflops(dev, M, N, K)}
+
+
+def dense_bf16_tflops(dev, M, N, K, reps=20):
+    """Context only: the vendor library's dense bf16 GEMM (torch.matmul ->
+    hipBLASLt) on the same shape and random operands, TFLOP/s."""
+    import torch
+
+    a = torch.randn(M, K, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(K, N, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    del c
+    return 2.0 * M * N * K / (e0.elapsed_time(e1) / reps) / 1e9
+
+
+def copy_gbs(dev, nbytes=256 << 20, reps=10):
+    """Context only: a plain device-to-device copy (torch), GB/s counting the
+    read and the write."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = [torch.empty_like(src) for _ in range(2)]
+    dst[0].copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        dst[i & 1].copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2.0 * nbytes / (e0.elapsed_time(e1) / reps) / 1e6
 
 
 def run_quant_act(nv, args, dev, M=7040, K=3072):
@@ -253,9 +292,14 @@ def run_ffn(nv, args, dev):
     ws = torch.empty(nv.quantize_workspace_bytes(M, F), dtype=torch.uint8, device=dev)
     Y = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
 
+    amax = torch.zeros(1, dtype=torch.float32, device=dev)
+
     def step(i):
-        nv.gemm_w4a4(qx, qu, out=H)
-        nv.quantize(H, out=qh, workspace=ws)
+        # the up projection's epilogue emits max|H|, so the requantize of H
+        # skips its amax pass
+        amax.zero_()
+        nv.gemm_w4a4(qx, qu, out=H, amax_out=amax)
+        nv.quantize(H, out=qh, workspace=ws, amax_in=amax)
         nv.gemm_w4a4(qh, qd, out=Y)
 
     ms, wall = time_steps(step, args.steps, args.warmup)
@@ -369,13 +413,15 @@ def main():
         sec["gemm_w4a4_7040x3072x3072_bf16"] = {
             "TFLOP/s": round(g["tflops"], 1), "frac_mfma_peak": round(g["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
             "kernel_TFLOP/s": round(g["kernel_tflops"], 1), "ms": round(g["ms"], 4),
-            "peak_TFLOP/s": MFMA_F16_PEAK_TFLOPS}
+            "peak_TFLOP/s": MFMA_F16_PEAK_TFLOPS,
+            "context_dense_bf16_hipblaslt_TFLOP/s": round(g["dense_bf16_tflops"], 1)}
         q = run_quant_act(nv, argparse.Namespace(steps=30, warmup=5, sets=args.sets), dev)
         sec["quantize_act_7040x3072_bf16"] = {
             "GB/s": round(q["gbs"], 1), "frac_hbm_peak": round(q["gbs"] / HBM_PEAK_GBS, 4),
             "us": round(q["ms"] * 1e3, 2),
             "kernels_us": {k: round(v[1] * 1e3, 2) for k, v in q["kernels"].items()}}
         out["secondary"] = sec
+        out["context_copy_GB/s"] = round(copy_gbs(dev), 1)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_kv()

@@ -136,10 +136,16 @@ int nvfp4_dequantize(const nvfp4_tensor *in, void *y, int32_t y_dtype, void *str
  * with A_hat = V * E4M3 scale (exact), likewise W_hat; fp32 accumulation.
  *   a: 1-D layout, [M, K].   w: 2-D layout, [N, K] (rows = output features).
  *   y: device, contiguous [M, N] in F32 or BF16 (nearest-even).
+ *   amax_out: NULL, or a device fp32 that the call raises to
+ *     max(*amax_out, max |y| over the stored y values) -- the tensor amax the
+ *     next quantize of y needs (pass it as that call's amax_in to skip its
+ *     amax pass; same result bit for bit).  The caller sets *amax_out before
+ *     the call (0 for a fresh maximum).  Updated with an atomic max on the
+ *     fp32 bit pattern, which orders non-negative values correctly.
  * K % 16 == 0, N % 16 == 0, any M >= 0.
  */
 int nvfp4_gemm_w4a4(const nvfp4_tensor *a, const nvfp4_tensor *w, void *y, int32_t y_dtype,
-                    void *stream);
+                    float *amax_out, void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* KV-cache ring                                                              */

@@ -71,7 +71,7 @@ _EXPORTS = {
                         C.c_void_p, C.c_size_t, C.c_void_p], C.c_int),
     "nvfp4_dequantize": ([C.POINTER(CTensor), C.c_void_p, C.c_int32, C.c_void_p], C.c_int),
     "nvfp4_gemm_w4a4": ([C.POINTER(CTensor), C.POINTER(CTensor), C.c_void_p, C.c_int32,
-                         C.c_void_p], C.c_int),
+                         C.c_void_p, C.c_void_p], C.c_int),
     "nvfp4_kv_ring_bytes": ([C.POINTER(CKvConfig)], C.c_size_t),
     "nvfp4_kv_store_workspace_bytes": ([C.POINTER(CKvConfig)], C.c_size_t),
     "nvfp4_kv_ring_init": ([C.POINTER(CKvRing), C.POINTER(CKvConfig), C.c_void_p, C.c_size_t],
@@ -203,12 +203,20 @@ def dequantize(t: NVFP4Tensor, dtype=torch.bfloat16, out: torch.Tensor | None = 
 
 
 def gemm_w4a4(a: NVFP4Tensor, w: NVFP4Tensor, out_dtype=torch.bfloat16,
-              out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """nvfp4_gemm_w4a4: Y[M, N] = s_A s_W A_hat W_hat^T (A 1-D, W 2-D)."""
+              out: torch.Tensor | None = None, amax_out: torch.Tensor | None = None,
+              stream=None) -> torch.Tensor:
+    """nvfp4_gemm_w4a4: Y[M, N] = s_A s_W A_hat W_hat^T (A 1-D, W 2-D).
+
+    amax_out: optional one-element float32 device tensor, raised to
+    max(amax_out, max|Y|) (set it to 0 first for a fresh maximum)."""
     if out is None:
         out = torch.empty((a.rows, w.rows), dtype=out_dtype, device=a.codes.device)
+    if amax_out is not None and (amax_out.dtype != torch.float32 or amax_out.numel() != 1
+                                 or not amax_out.is_cuda):
+        raise ValueError("amax_out must be a one-element float32 device tensor")
     ca, cw = a.c(), w.c()
     _check(lib().nvfp4_gemm_w4a4(C.byref(ca), C.byref(cw), _dev(out, "out"), _DT[out.dtype],
+                                 None if amax_out is None else amax_out.data_ptr(),
                                  _stream(stream)))
     return out
 

@@ -229,7 +229,7 @@ int nvfp4_dequantize(const nvfp4_tensor *in, void *y, int32_t y_dtype, void *str
 }
 
 int nvfp4_gemm_w4a4(const nvfp4_tensor *a, const nvfp4_tensor *w, void *y, int32_t y_dtype,
-                    void *stream) {
+                    float *amax_out, void *stream) {
     int st = check_tensor(a, "gemm A");
     if (st) return st;
     st = check_tensor(w, "gemm W");
@@ -245,9 +245,10 @@ int nvfp4_gemm_w4a4(const nvfp4_tensor *a, const nvfp4_tensor *w, void *y, int32
         return fail(NVFP4_EINVAL, "gemm: bad y dtype %d", y_dtype);
     if (a->rows * w->rows > 0 && !y) return fail(NVFP4_EINVAL, "gemm: NULL y");
     if (!aligned16(y)) return fail(NVFP4_EALIGN, "gemm: y not 16-byte aligned");
+    if (((uintptr_t)amax_out & 3u)) return fail(NVFP4_EALIGN, "gemm: amax_out misaligned");
     hipError_t e = nvfp4::launch_gemm_w4a4(a->codes, a->scales, a->s_dec, w->codes, w->scales,
                                            w->s_dec, a->rows, w->rows, a->cols, y, y_dtype,
-                                           (hipStream_t)stream);
+                                           amax_out, (hipStream_t)stream);
     return hip_status(e, "gemm launch");
 }
 

@@ -267,7 +267,8 @@ __device__ __forceinline__ void step_all(f32x16 (&acc)[FM][FN], const Frag (&A)[
 template <bool OUT_BF16, bool KFAST>
 __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float *__restrict__ a_sdec,
                                                         const float *__restrict__ w_sdec,
-                                                        void *__restrict__ yv) {
+                                                        void *__restrict__ yv,
+                                                        float *__restrict__ amax_out) {
     const int64_t M = g.M, N = g.N, K = g.K;
     const int64_t tn_count = (N + BN - 1) / BN;
     const int64_t ntiles = ((M + BM - 1) / BM) * tn_count;
@@ -345,6 +346,7 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
     if (!active) return;
 
     const float scale = (*a_sdec) * (*w_sdec);
+    float amax = 0.0f;  // max |stored y| of this lane
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -356,19 +358,27 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
                 const int64_t row = rbase + (e >> 2) * 8 + (e & 3);
                 const float v = scale * acc[i][j][e];
                 if (row < M && col < N) {
-                    if (OUT_BF16)
-                        ((__bf16 *)yv)[row * N + col] = (__bf16)v;
-                    else
+                    if (OUT_BF16) {
+                        const __bf16 b = (__bf16)v;
+                        ((__bf16 *)yv)[row * N + col] = b;
+                        amax = fmaxf(amax, fabsf((float)b));
+                    } else {
                         ((float *)yv)[row * N + col] = v;
+                        amax = fmaxf(amax, fabsf(v));
+                    }
                 }
             }
         }
+    if (amax_out) {
+        amax = wave_max(amax);
+        if (lane == 0) atomicMax((unsigned int *)amax_out, __float_as_uint(amax));
+    }
 }
 
 hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_sdec,
                             const uint8_t *w_codes, const uint8_t *w_scales,
                             const float *w_sdec, int64_t M, int64_t N, int64_t K, void *y,
-                            int ydtype, hipStream_t s) {
+                            int ydtype, float *amax_out, hipStream_t s) {
     if (M == 0 || N == 0) return hipSuccess;
     const int64_t ntiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const dim3 grid((unsigned)ntiles);
@@ -389,7 +399,7 @@ hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, con
     }
 #define NVFP4_GEMM(BF, KF)                                                                  \
     NVFP4_LAUNCH("gemm_w4a4", (gemm_w4a4_kernel<BF, KF>), grid, dim3(256), KF ? kLdsBytes : 0, \
-                 s, g, a_sdec, w_sdec, y)
+                 s, g, a_sdec, w_sdec, y, amax_out)
     if (ydtype == kBF16) {
         if (fast)
             NVFP4_GEMM(true, true);

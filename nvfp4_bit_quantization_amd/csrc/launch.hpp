@@ -92,6 +92,6 @@ hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
 hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_sdec,
                             const uint8_t *w_codes, const uint8_t *w_scales,
                             const float *w_sdec, int64_t M, int64_t N, int64_t K, void *y,
-                            int ydtype, hipStream_t s);
+                            int ydtype, float *amax_out, hipStream_t s);
 
 }  // namespace nvfp4

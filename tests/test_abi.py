@@ -78,12 +78,13 @@ def test_dequantize_and_gemm_validation(L):
     assert L.nvfp4_dequantize(C.byref(t), FAKE, 9, None) == -1
     assert L.nvfp4_dequantize(C.byref(t), FAKE + 2, 1, None) == -2
     a, w = tensor(64, 64), tensor(32, 64, nv.LAYOUT_2D)
-    assert L.nvfp4_gemm_w4a4(C.byref(w), C.byref(w), FAKE, 1, None) == -1  # A must be 1-D
-    assert L.nvfp4_gemm_w4a4(C.byref(a), C.byref(a), FAKE, 1, None) == -1  # W must be 2-D
+    assert L.nvfp4_gemm_w4a4(C.byref(w), C.byref(w), FAKE, 1, None, None) == -1  # A must be 1-D
+    assert L.nvfp4_gemm_w4a4(C.byref(a), C.byref(a), FAKE, 1, None, None) == -1  # W must be 2-D
     w2 = tensor(32, 128, nv.LAYOUT_2D)
-    assert L.nvfp4_gemm_w4a4(C.byref(a), C.byref(w2), FAKE, 1, None) == -3
-    assert L.nvfp4_gemm_w4a4(C.byref(a), C.byref(w), FAKE, 4, None) == -1
-    assert L.nvfp4_gemm_w4a4(C.byref(a), C.byref(w), None, 1, None) == -1
+    assert L.nvfp4_gemm_w4a4(C.byref(a), C.byref(w2), FAKE, 1, None, None) == -3
+    assert L.nvfp4_gemm_w4a4(C.byref(a), C.byref(w), FAKE, 4, None, None) == -1
+    assert L.nvfp4_gemm_w4a4(C.byref(a), C.byref(w), None, 1, None, None) == -1
+    assert L.nvfp4_gemm_w4a4(C.byref(a), C.byref(w), FAKE, 1, FAKE + 2, None) == -2  # amax_out
 
 
 CFG = nv.KVConfig()

@@ -120,3 +120,30 @@ def test_gemm_deterministic(nv, orc):
     y2 = nv.gemm_w4a4(a, w, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("K", [512, 272])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_gemm_amax_out(nv, orc, K, out_dtype):
+    """amax_out is max|Y| of the stored values (bit-exact), so requantizing Y
+    with it as amax_in gives the same codes, scales and s_dec as a plain
+    quantize of Y."""
+    print("case: gemm amax_out", K, out_dtype, flush=True)
+    qa, qw = operands(orc, 300, 272, K, 1005)
+    a = upload(nv, *qa, 0)
+    w = upload(nv, *qw, 1)
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    y = nv.gemm_w4a4(a, w, out_dtype=out_dtype, amax_out=amax)
+    ref = y.float().abs().max()
+    torch.cuda.synchronize()
+    assert amax.item() == ref.item() and amax.item() > 0
+    q1 = nv.quantize(y)
+    q2 = nv.quantize(y, amax_in=amax)
+    torch.cuda.synchronize()
+    assert q1.s_dec == q2.s_dec
+    assert torch.equal(q1.codes, q2.codes) and torch.equal(q1.scales, q2.scales)
+    # a larger preset value is kept
+    big = torch.full((1,), 1e30, dtype=torch.float32, device="cuda")
+    nv.gemm_w4a4(a, w, out_dtype=out_dtype, amax_out=big)
+    torch.cuda.synchronize()
+    assert big.item() == np.float32(1e30)
