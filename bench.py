@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
+MFMA_FP4_PEAK_TFLOPS = 10100.0
 METRIC = "NVFP4 quant/dequant GB/s (% HBM peak); W4A4 GEMM TFLOP/s (% bf16 MFMA peak)"
 
 
@@ -212,9 +213,42 @@ def run_gemm_attn(nv, args, dev):
     kt = kernel_times(nv, step, max(5, args.steps // 5), 0)
     flops = 2.0 * M * N * K
     kms = kt["gemm_w4a4"][1]
-    return {"ms": ms, "wall_ms": wall, "tflops": flops / ms / 1e9, "kernel_ms": kms,
-            "kernel_tflops": flops / kms / 1e9, "flops": flops, "kernels": kt,
-            "dense_bf16_tflops": dense_bf16_tflops(dev, M, N, K)}
+    out = {"ms": ms, "wall_ms": wall, "tflops": flops / ms / 1e9, "kernel_ms": kms,
+           "kernel_tflops": flops / kms / 1e9, "flops": flops, "kernels": kt,
+           "dense_bf16_tflops": dense_bf16_tflops(dev, M, N, K)}
+    out.update(mx_comparison(nv, args, dev, X, Y, M, N, K))
+    return out
+
+
+def mx_comparison(nv, args, dev, X, Y, M, N, K, nrows=64):
+    """The MXFP4 speed reference on the same bf16 operands (E8M0 scale per
+    32, native scaled FP4 MFMA), and the relative Frobenius error of both
+    formats against the fp64 product of the unquantized operands on `nrows`
+    sampled rows (first and last included)."""
+    import numpy as np
+    import torch
+
+    import synth
+
+    W = torch.from_numpy(synth.weights(1003, 1, N, K)).to(dev).to(torch.bfloat16)
+    qa, qw = nv.mx_quantize(X), nv.mx_quantize(W)
+    Ym = torch.empty_like(Y)
+
+    def step(i):
+        nv.gemm_mx(qa, qw, out=Ym)
+
+    ms, _ = time_steps(step, args.steps, args.warmup)
+    kt = kernel_times(nv, step, max(5, args.steps // 5), 0)
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(5).integers(0, M, nrows - 2)]))
+    x = X.float().cpu().numpy().astype(np.float64)[rows]
+    w = W.float().cpu().numpy().astype(np.float64)
+    ref = x @ w.T
+    nrm = np.linalg.norm(ref)
+    err_nv = np.linalg.norm(Y.float().cpu().numpy().astype(np.float64)[rows] - ref) / nrm
+    err_mx = np.linalg.norm(Ym.float().cpu().numpy().astype(np.float64)[rows] - ref) / nrm
+    return {"mx_ms": ms, "mx_kernel_ms": kt["gemm_mx"][1],
+            "mx_kernel_tflops": 2.0 * M * N * K / kt["gemm_mx"][1] / 1e9,
+            "rel_err_nvfp4": float(err_nv), "rel_err_mxfp4": float(err_mx)}
 
 
 def dense_bf16_tflops(dev, M, N, K, reps=20):
@@ -414,7 +448,14 @@ def main():
             "TFLOP/s": round(g["tflops"], 1), "frac_mfma_peak": round(g["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
             "kernel_TFLOP/s": round(g["kernel_tflops"], 1), "ms": round(g["ms"], 4),
             "peak_TFLOP/s": MFMA_F16_PEAK_TFLOPS,
-            "context_dense_bf16_hipblaslt_TFLOP/s": round(g["dense_bf16_tflops"], 1)}
+            "context_dense_bf16_hipblaslt_TFLOP/s": round(g["dense_bf16_tflops"], 1),
+            "rel_err_vs_fp64_unquantized": round(g["rel_err_nvfp4"], 5)}
+        sec["mxfp4_reference_gemm_7040x3072x3072_bf16"] = {
+            "kernel_TFLOP/s": round(g["mx_kernel_tflops"], 1),
+            "peak_TFLOP/s": MFMA_FP4_PEAK_TFLOPS,
+            "frac_fp4_mfma_peak": round(g["mx_kernel_tflops"] / MFMA_FP4_PEAK_TFLOPS, 4),
+            "rel_err_vs_fp64_unquantized": round(g["rel_err_mxfp4"], 5),
+            "note": "E8M0 scale per 32 elements: a different quantization, not NVFP4"}
         q = run_quant_act(nv, argparse.Namespace(steps=30, warmup=5, sets=args.sets), dev)
         sec["quantize_act_7040x3072_bf16"] = {
             "GB/s": round(q["gbs"], 1), "frac_hbm_peak": round(q["gbs"] / HBM_PEAK_GBS, 4),

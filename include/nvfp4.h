@@ -148,6 +148,39 @@ int nvfp4_gemm_w4a4(const nvfp4_tensor *a, const nvfp4_tensor *w, void *y, int32
                     float *amax_out, void *stream);
 
 /* ------------------------------------------------------------------------ */
+/* MXFP4 speed reference (not part of the method)                            */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The W4A4 GEMM is measured beside the gfx950 MFMA that takes FP4 operands
+ * with power-of-two block scales: MXFP4 of the OCP Microscaling Formats
+ * (MX) v1.0 specification -- E2M1 elements, one E8M0 scale (2^(byte - 127))
+ * per 32 consecutive elements along a row.  NVFP4 operands cannot use that
+ * instruction (E4M3 scale with mantissa bits, 16-element blocks, products
+ * of up to 6 significant bits), so the MX result is a different
+ * quantization of the same data, compared for speed and error only.
+ *
+ * nvfp4_mx_quantize: x (device, F32 or BF16, contiguous [rows, cols],
+ *   cols % 32 == 0) -> codes [rows, cols/2] (element 2j in the low nibble of
+ *   byte j) and scales [rows, cols/32] E8M0 bytes, all caller-owned device
+ *   memory.  Per block: e = floor(log2(amax)) - 2 clamped to [-127, 127]
+ *   (a subnormal amax gives -127), scale byte e + 127 (0 for an all-zero
+ *   block), elements E2M1(RN(x * 2^-e)) saturating at 6.
+ */
+int nvfp4_mx_quantize(const void *x, int32_t x_dtype, int64_t rows, int64_t cols,
+                      uint8_t *codes, uint8_t *scales, void *stream);
+
+/*
+ * nvfp4_gemm_mx: Y[m, n] = sum_k A_mx[m, k] * W_mx[n, k] with fp32
+ * accumulation (v_mfma_scale_f32_32x32x64_f8f6f4); A [M, K] and W [N, K] as
+ * written by nvfp4_mx_quantize; y device [M, N] F32 or BF16 (nearest-even).
+ * K % 256 == 0, M, N >= 0; each code array below 2^31 bytes.
+ */
+int nvfp4_gemm_mx(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *w_codes,
+                  const uint8_t *w_scales, int64_t M, int64_t N, int64_t K, void *y,
+                  int32_t y_dtype, void *stream);
+
+/* ------------------------------------------------------------------------ */
 /* KV-cache ring                                                              */
 /* ------------------------------------------------------------------------ */
 

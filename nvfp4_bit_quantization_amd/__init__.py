@@ -72,6 +72,10 @@ _EXPORTS = {
     "nvfp4_dequantize": ([C.POINTER(CTensor), C.c_void_p, C.c_int32, C.c_void_p], C.c_int),
     "nvfp4_gemm_w4a4": ([C.POINTER(CTensor), C.POINTER(CTensor), C.c_void_p, C.c_int32,
                          C.c_void_p, C.c_void_p], C.c_int),
+    "nvfp4_mx_quantize": ([C.c_void_p, C.c_int32, C.c_int64, C.c_int64, C.c_void_p,
+                           C.c_void_p, C.c_void_p], C.c_int),
+    "nvfp4_gemm_mx": ([C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_int64,
+                       C.c_int64, C.c_void_p, C.c_int32, C.c_void_p], C.c_int),
     "nvfp4_kv_ring_bytes": ([C.POINTER(CKvConfig)], C.c_size_t),
     "nvfp4_kv_store_workspace_bytes": ([C.POINTER(CKvConfig)], C.c_size_t),
     "nvfp4_kv_ring_init": ([C.POINTER(CKvRing), C.POINTER(CKvConfig), C.c_void_p, C.c_size_t],
@@ -218,6 +222,38 @@ def gemm_w4a4(a: NVFP4Tensor, w: NVFP4Tensor, out_dtype=torch.bfloat16,
     _check(lib().nvfp4_gemm_w4a4(C.byref(ca), C.byref(cw), _dev(out, "out"), _DT[out.dtype],
                                  None if amax_out is None else amax_out.data_ptr(),
                                  _stream(stream)))
+    return out
+
+
+# --------------------------------------------------------------------------
+# MXFP4 speed reference (not part of the method)
+# --------------------------------------------------------------------------
+
+def mx_quantize(x: torch.Tensor, stream=None):
+    """nvfp4_mx_quantize: x [rows, cols] (float32 or bfloat16, cols % 32 == 0)
+    -> (codes uint8 [rows, cols/2], scales uint8 [rows, cols/32] E8M0)."""
+    if x.dim() != 2 or x.dtype not in _DT:
+        raise ValueError("mx_quantize expects a 2-D float32 or bfloat16 tensor")
+    x = x.contiguous()
+    rows, cols = x.shape
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, max(cols // 32, 0)), dtype=torch.uint8, device=x.device)
+    _check(lib().nvfp4_mx_quantize(_dev(x, "x"), _DT[x.dtype], rows, cols, codes.data_ptr(),
+                                   scales.data_ptr(), _stream(stream)))
+    return codes, scales
+
+
+def gemm_mx(a, w, out_dtype=torch.bfloat16, out: torch.Tensor | None = None,
+            stream=None) -> torch.Tensor:
+    """nvfp4_gemm_mx: Y = A_mx W_mx^T for (codes, scales) pairs from mx_quantize."""
+    (ac, as_), (wc, ws) = a, w
+    M, N, K = ac.shape[0], wc.shape[0], ac.shape[1] * 2
+    if wc.shape[1] * 2 != K:
+        raise ValueError("gemm_mx: K mismatch")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=ac.device)
+    _check(lib().nvfp4_gemm_mx(ac.data_ptr(), as_.data_ptr(), wc.data_ptr(), ws.data_ptr(), M, N,
+                               K, _dev(out, "out"), _DT[out.dtype], _stream(stream)))
     return out
 
 

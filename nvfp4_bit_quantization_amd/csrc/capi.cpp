@@ -252,6 +252,44 @@ int nvfp4_gemm_w4a4(const nvfp4_tensor *a, const nvfp4_tensor *w, void *y, int32
     return hip_status(e, "gemm launch");
 }
 
+// ---- MXFP4 speed reference ------------------------------------------------------
+
+int nvfp4_mx_quantize(const void *x, int32_t x_dtype, int64_t rows, int64_t cols,
+                      uint8_t *codes, uint8_t *scales, void *stream) {
+    if (rows < 0 || cols < 0) return fail(NVFP4_ESHAPE, "mx_quantize: negative shape");
+    if (cols % 32) return fail(NVFP4_ESHAPE, "mx_quantize: cols %% 32 != 0 (got %lld)",
+                               (long long)cols);
+    if (x_dtype != NVFP4_DTYPE_F32 && x_dtype != NVFP4_DTYPE_BF16)
+        return fail(NVFP4_EINVAL, "mx_quantize: bad x dtype %d", x_dtype);
+    if (rows * cols == 0) return ok();
+    if (!x || !codes || !scales) return fail(NVFP4_EINVAL, "mx_quantize: NULL pointer");
+    if (!aligned16(x) || !aligned16(codes))
+        return fail(NVFP4_EALIGN, "mx_quantize: x and codes must be 16-byte aligned");
+    hipError_t e = nvfp4::launch_mx_quantize(x, x_dtype, rows, cols, codes, scales,
+                                             (hipStream_t)stream);
+    return hip_status(e, "mx_quantize launch");
+}
+
+int nvfp4_gemm_mx(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *w_codes,
+                  const uint8_t *w_scales, int64_t M, int64_t N, int64_t K, void *y,
+                  int32_t y_dtype, void *stream) {
+    if (M < 0 || N < 0 || K <= 0) return fail(NVFP4_ESHAPE, "gemm_mx: bad shape");
+    if (K % 256) return fail(NVFP4_ESHAPE, "gemm_mx: K %% 256 != 0 (got %lld)", (long long)K);
+    if (M * (K / 2) >= ((int64_t)1 << 31) || N * (K / 2) >= ((int64_t)1 << 31))
+        return fail(NVFP4_ESHAPE, "gemm_mx: code arrays must stay below 2^31 bytes");
+    if (y_dtype != NVFP4_DTYPE_F32 && y_dtype != NVFP4_DTYPE_BF16)
+        return fail(NVFP4_EINVAL, "gemm_mx: bad y dtype %d", y_dtype);
+    if (M * N == 0) return ok();
+    if (!a_codes || !a_scales || !w_codes || !w_scales || !y)
+        return fail(NVFP4_EINVAL, "gemm_mx: NULL pointer");
+    if (!aligned16(a_codes) || !aligned16(w_codes) || !aligned16(y) || !aligned16(a_scales) ||
+        !aligned16(w_scales))
+        return fail(NVFP4_EALIGN, "gemm_mx: device pointers must be 16-byte aligned");
+    hipError_t e = nvfp4::launch_gemm_mx(a_codes, a_scales, w_codes, w_scales, M, N, K, y,
+                                         y_dtype, (hipStream_t)stream);
+    return hip_status(e, "gemm_mx launch");
+}
+
 // ---- KV ring ------------------------------------------------------------------
 
 size_t nvfp4_kv_ring_bytes(const nvfp4_kv_config *cfg) {

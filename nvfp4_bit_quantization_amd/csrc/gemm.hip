@@ -66,6 +66,7 @@ constexpr int kLdsBytes = 2 * kStage;
 static_assert(kStage % 256 == 0, "stage alignment");
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void *lvoid;  // LDS
 
 struct GemmArgs {
@@ -185,6 +186,7 @@ struct StageSrc {
     uint32_t a[BM / 32], w[BN / 32], asr, wsr;
 };
 
+template <bool SCALES>
 __device__ __forceinline__ void stage_src(StageSrc &q, const GemmArgs &g, int64_t m0, int64_t n0,
                                           int wave, int lane) {
     const int64_t kbytes = g.K >> 1, KB = g.K >> 4;
@@ -192,10 +194,12 @@ __device__ __forceinline__ void stage_src(StageSrc &q, const GemmArgs &g, int64_
                                              kBufferWord3);
     q.wc = __builtin_amdgcn_make_buffer_rsrc((void *)g.w_codes, (short)0, (int)(g.N * kbytes),
                                              kBufferWord3);
-    q.as = __builtin_amdgcn_make_buffer_rsrc((void *)g.a_scales, (short)0, (int)(g.M * KB),
-                                             kBufferWord3);
-    q.ws = __builtin_amdgcn_make_buffer_rsrc((void *)g.w_scales, (short)0,
-                                             (int)((g.N >> 4) * KB), kBufferWord3);
+    if (SCALES) {
+        q.as = __builtin_amdgcn_make_buffer_rsrc((void *)g.a_scales, (short)0, (int)(g.M * KB),
+                                                 kBufferWord3);
+        q.ws = __builtin_amdgcn_make_buffer_rsrc((void *)g.w_scales, (short)0,
+                                                 (int)((g.N >> 4) * KB), kBufferWord3);
+    }
     const int rib = lane >> 3, gcol = (lane & 7) ^ rib;
 #pragma unroll
     for (int bb = 0; bb < BM / 32; ++bb) {
@@ -215,7 +219,9 @@ __device__ __forceinline__ void stage_src(StageSrc &q, const GemmArgs &g, int64_
     q.wsr = (uint32_t)((gr0 < glast ? gr0 : glast) * KB);
 }
 
-// Issue this wave's direct-to-LDS loads of K step kt into `stage`.
+// Issue this wave's direct-to-LDS loads of K step kt into `stage` (codes,
+// and with SCALES the NVFP4 block scales).
+template <bool SCALES>
 __device__ __forceinline__ void stage_load(const StageSrc &q, uint8_t *stage, int64_t kt, int wave,
                                            int lane) {
     const uint32_t kc = (uint32_t)kt * 128, ks = (uint32_t)kt * 16;
@@ -227,6 +233,7 @@ __device__ __forceinline__ void stage_load(const StageSrc &q, uint8_t *stage, in
     for (int bb = 0; bb < BN / 32; ++bb)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             q.wc, (lvoid)(stage + kBOff + (wave * (BN / 32) + bb) * 1024), 16, q.w[bb], kc, 0, 0);
+    if (!SCALES) return;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(q.as, (lvoid)(stage + kASOff + wave * 1024), 16,
                                              q.asr, ks, 0, 0);
     if (wave == 0 && lane < BN / 16)
@@ -237,15 +244,18 @@ __device__ __forceinline__ void stage_load(const StageSrc &q, uint8_t *stage, in
 // The wave's fragments of one K step from LDS: lane (r, h) reads, for each
 // fragment row R, the 16-byte columns 4h .. 4h + 3 (un-swizzled) and the 8
 // scale bytes of its half.
+template <bool SCALES>
 __device__ __forceinline__ void stage_read(Frag (&A)[FM], Frag (&B)[FN], const uint8_t *stage,
                                            int wm, int wn, int r, int h) {
     const int rib = r & 7;
+    if (SCALES) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-        A[i].sc = *(const u32x2 *)(stage + kASOff + (wm * WM + i * 32 + r) * 16 + h * 8);
+        for (int i = 0; i < FM; ++i)
+            A[i].sc = *(const u32x2 *)(stage + kASOff + (wm * WM + i * 32 + r) * 16 + h * 8);
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-        B[j].sc = *(const u32x2 *)(stage + kBSOff + ((wn * WN + j * 32 + r) >> 4) * 16 + h * 8);
+        for (int j = 0; j < FN; ++j)
+            B[j].sc = *(const u32x2 *)(stage + kBSOff + ((wn * WN + j * 32 + r) >> 4) * 16 + h * 8);
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const int slot = ((h * 4 + c) ^ rib) * 16 + rib * 128;
@@ -301,8 +311,8 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
     if (KFAST) {
         extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
         StageSrc src;
-        stage_src(src, g, m0, n0, wave, lane);
-        stage_load(src, lds, 0, wave, lane);
+        stage_src<true>(src, g, m0, n0, wave, lane);
+        stage_load<true>(src, lds, 0, wave, lane);
         // Each iteration: this wave's loads of step kt have landed; after the
         // barrier so have everyone's, and nobody still reads the stage that
         // the loads of step kt + 1 overwrite.  The last iteration reloads its
@@ -313,8 +323,8 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __syncthreads();
                 const int64_t kn = kt + 1 < nk ? kt + 1 : kt;
-                stage_read(A, B, lds + (kt & 1) * kStage, wm, wn, r, h);
-                stage_load(src, lds + ((kt + 1) & 1) * kStage, kn, wave, lane);
+                stage_read<true>(A, B, lds + (kt & 1) * kStage, wm, wn, r, h);
+                stage_load<true>(src, lds + ((kt + 1) & 1) * kStage, kn, wave, lane);
                 step_all(acc, A, B, std::make_integer_sequence<int, NSUB>{});
             }
         } else {
@@ -322,7 +332,7 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __syncthreads();
                 const int64_t kn = kt + 1 < nk ? kt + 1 : kt;
-                stage_load(src, lds + ((kt + 1) & 1) * kStage, kn, wave, lane);
+                stage_load<true>(src, lds + ((kt + 1) & 1) * kStage, kn, wave, lane);
             }
         }
         // no load into LDS is still in flight when the wave leaves
@@ -412,6 +422,158 @@ hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, con
             NVFP4_GEMM(false, false);
     }
 #undef NVFP4_GEMM
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// MXFP4 reference GEMM (speed reference, not part of the method)
+// ---------------------------------------------------------------------------
+//
+// OCP Microscaling (MX) v1.0 MXFP4: E2M1 elements with one power-of-two E8M0
+// scale per 32 consecutive elements (1-D along K for both operands).  gfx950
+// multiplies such operands natively: v_mfma_scale_f32_32x32x64_f8f6f4 with
+// fp4 A and B takes the packed codes as they are and one E8M0 byte per lane
+// per 32 K values.  Lane half h holds K [128 h, 128 h + 128) of a 256-deep
+// step as in the NVFP4 kernel, so MFMA substep s (64 K) pairs dwords
+// 4s .. 4s + 3 of both halves, each half with its own block scale (byte s of
+// the half's scale dword).  Codes are staged through LDS exactly as for
+// NVFP4; the scale dword of each fragment is loaded from memory per step.
+// Y = sum_k A_mx[m, k] * W_mx[n, k], fp32 accumulation, no tensor scale.
+//
+// The NVFP4 operands cannot run on this instruction: an E4M3 block scale
+// has 3 mantissa bits (E8M0 is a pure power of two), covers 16 elements
+// (two per MX block), and E2M1 x E4M3 needs up to 6 significant bits, which
+// no FP4/FP6/FP8 element times a power of two holds.
+
+template <int S>
+__device__ __forceinline__ void mx_substep(f32x16 (&acc)[FM][FN], const Frag (&A)[FM],
+                                           const Frag (&B)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const u32x4 qa = A[i].q[S], qb = B[j].q[S];
+            const i32x8 a = {(int)qa.x, (int)qa.y, (int)qa.z, (int)qa.w, 0, 0, 0, 0};
+            const i32x8 b = {(int)qb.x, (int)qb.y, (int)qb.z, (int)qb.w, 0, 0, 0, 0};
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                a, b, acc[i][j], 4, 4, S, (int)A[i].sc.x, S, (int)B[j].sc.x);
+        }
+}
+
+template <int... S>
+__device__ __forceinline__ void mx_step(f32x16 (&acc)[FM][FN], const Frag (&A)[FM],
+                                        const Frag (&B)[FN], std::integer_sequence<int, S...>) {
+    (mx_substep<S>(acc, A, B), ...);
+}
+
+// g.a_scales / g.w_scales hold the E8M0 bytes, [rows, K / 32].  K % 256 == 0.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs g, void *__restrict__ yv) {
+    const int64_t M = g.M, N = g.N, K = g.K;
+    const int64_t tn_count = (N + BN - 1) / BN;
+    const int64_t ntiles = ((M + BM - 1) / BM) * tn_count;
+    const int64_t b = blockIdx.x;
+    const int64_t per = ntiles / kXcds;
+    const int64_t t = b < per * kXcds ? (b % kXcds) * per + b / kXcds : b;
+    const int64_t m0 = (t / tn_count) * BM, n0 = (t % tn_count) * BN;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = lane >> 5, r = lane & 31, wm = wave >> 1, wn = wave & 1;
+    const int64_t mw = m0 + wm * WM, nw = n0 + wn * WN;
+    const bool active = mw < M && nw < N;
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    // scale dword of each fragment row: bytes 8 kt + 4 h .. +3 of the row
+    const int64_t SB = K >> 5;
+    const uint8_t *sa[FM], *sb[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int64_t row = mw + i * 32 + r < M ? mw + i * 32 + r : M - 1;
+        sa[i] = g.a_scales + row * SB + h * 4;
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int64_t row = nw + j * 32 + r < N ? nw + j * 32 + r : N - 1;
+        sb[j] = g.w_scales + row * SB + h * 4;
+    }
+
+    const int64_t nk = K / BK;
+    Frag A[FM], B[FN];
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    StageSrc src;
+    stage_src<false>(src, g, m0, n0, wave, lane);
+    stage_load<false>(src, lds, 0, wave, lane);
+    if (active) {
+        for (int64_t kt = 0; kt < nk; ++kt) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            const int64_t kn = kt + 1 < nk ? kt + 1 : kt;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) A[i].sc.x = *(const uint32_t *)(sa[i] + kt * 8);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) B[j].sc.x = *(const uint32_t *)(sb[j] + kt * 8);
+            stage_read<false>(A, B, lds + (kt & 1) * kStage, wm, wn, r, h);
+            stage_load<false>(src, lds + ((kt + 1) & 1) * kStage, kn, wave, lane);
+            mx_step(acc, A, B, std::make_integer_sequence<int, 4>{});
+        }
+    } else {
+        for (int64_t kt = 0; kt < nk; ++kt) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            const int64_t kn = kt + 1 < nk ? kt + 1 : kt;
+            stage_load<false>(src, lds + ((kt + 1) & 1) * kStage, kn, wave, lane);
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (!active) return;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int64_t col = nw + j * 32 + r;
+            const int64_t rbase = mw + i * 32 + h * 4;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t row = rbase + (e >> 2) * 8 + (e & 3);
+                if (row < M && col < N) {
+                    if (OUT_BF16)
+                        ((__bf16 *)yv)[row * N + col] = (__bf16)acc[i][j][e];
+                    else
+                        ((float *)yv)[row * N + col] = acc[i][j][e];
+                }
+            }
+        }
+}
+
+hipError_t launch_gemm_mx(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *w_codes,
+                          const uint8_t *w_scales, int64_t M, int64_t N, int64_t K, void *y,
+                          int ydtype, hipStream_t s) {
+    if (M == 0 || N == 0) return hipSuccess;
+    static bool attr_set = false;
+    if (!attr_set) {
+        const void *fns[2] = {(const void *)gemm_mx_kernel<true>, (const void *)gemm_mx_kernel<false>};
+        for (const void *f : fns) {
+            hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               kLdsBytes);
+            if (e != hipSuccess) return e;
+        }
+        attr_set = true;
+    }
+    const int64_t ntiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const GemmArgs g{a_codes, a_scales, w_codes, w_scales, M, N, K};
+    if (ydtype == kBF16)
+        NVFP4_LAUNCH("gemm_mx", gemm_mx_kernel<true>, dim3((unsigned)ntiles), dim3(256), kLdsBytes,
+                     s, g, y);
+    else
+        NVFP4_LAUNCH("gemm_mx", gemm_mx_kernel<false>, dim3((unsigned)ntiles), dim3(256), kLdsBytes,
+                     s, g, y);
     return hipGetLastError();
 }
 

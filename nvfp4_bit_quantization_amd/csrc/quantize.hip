@@ -335,4 +335,63 @@ hipError_t launch_dequant(const uint8_t *codes, const uint8_t *scales, const flo
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// MXFP4 quantize (OCP Microscaling v1.0; reference format for the MX GEMM)
+// ---------------------------------------------------------------------------
+
+// One lane per 32-element block along a row: shared exponent
+// e = floor(log2(amax)) - 2 (2 = the E2M1 maximum exponent), clamped to
+// [-127, 127] (0 for an all-zero block's scale byte), E8M0 byte e + 127;
+// elements E2M1(RN(x * 2^-e)) with saturation at 6.  A subnormal amax takes
+// e = -127.
+template <typename T>
+__global__ __launch_bounds__(256) void mx_quantize_kernel(const T *__restrict__ x, int64_t nblk,
+                                                          uint32_t *__restrict__ codes,
+                                                          uint8_t *__restrict__ scales) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += stride) {
+        typename Raw16Of<T>::type r0, r1;
+        load_raw16(x + b * 32, r0);
+        load_raw16(x + b * 32 + 16, r1);
+        float v[32];
+        float(&v0)[16] = *reinterpret_cast<float(*)[16]>(&v[0]);
+        float(&v1)[16] = *reinterpret_cast<float(*)[16]>(&v[16]);
+        unpack16(r0, v0);
+        unpack16(r1, v1);
+        float am = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(v[i]));
+        const int be = (int)((__float_as_uint(am) >> 23) & 0xFFu);
+        int e = be == 0 ? -127 : be - 127 - 2;
+        e = e < -127 ? -127 : (e > 127 ? 127 : e);
+        const float inv = __builtin_ldexpf(1.0f, -e);  // exact power of two
+        uint32_t q[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            uint32_t w = 0;
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * d] * inv, v[8 * d + 1] * inv, 1.0f, 0);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * d + 2] * inv, v[8 * d + 3] * inv, 1.0f, 1);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * d + 4] * inv, v[8 * d + 5] * inv, 1.0f, 2);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[8 * d + 6] * inv, v[8 * d + 7] * inv, 1.0f, 3);
+            q[d] = w;
+        }
+        *(u32x4 *)(codes + b * 4) = u32x4{q[0], q[1], q[2], q[3]};
+        scales[b] = (uint8_t)(am == 0.0f ? 0 : e + 127);
+    }
+}
+
+hipError_t launch_mx_quantize(const void *x, int xdtype, int64_t rows, int64_t cols,
+                              uint8_t *codes, uint8_t *scales, hipStream_t s) {
+    const int64_t nblk = rows * cols / 32;
+    if (nblk == 0) return hipSuccess;
+    const int g = grid_for(nblk, 256, 4096);
+    if (xdtype == kF32)
+        NVFP4_LAUNCH("mx_quantize", mx_quantize_kernel<float>, dim3(g), dim3(256), 0, s,
+                     (const float *)x, nblk, (uint32_t *)codes, scales);
+    else
+        NVFP4_LAUNCH("mx_quantize", mx_quantize_kernel<uint16_t>, dim3(g), dim3(256), 0, s,
+                     (const uint16_t *)x, nblk, (uint32_t *)codes, scales);
+    return hipGetLastError();
+}
+
 }  // namespace nvfp4

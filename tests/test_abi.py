@@ -87,6 +87,21 @@ def test_dequantize_and_gemm_validation(L):
     assert L.nvfp4_gemm_w4a4(C.byref(a), C.byref(w), FAKE, 1, FAKE + 2, None) == -2  # amax_out
 
 
+def test_mx_reference_validation(L):
+    # nvfp4_mx_quantize(x, dtype, rows, cols, codes, scales, stream)
+    assert L.nvfp4_mx_quantize(FAKE, 0, 4, 48, FAKE, FAKE, None) == -3      # cols % 32
+    assert L.nvfp4_mx_quantize(FAKE, 7, 4, 64, FAKE, FAKE, None) == -1      # dtype
+    assert L.nvfp4_mx_quantize(None, 0, 4, 64, FAKE, FAKE, None) == -1      # NULL x
+    assert L.nvfp4_mx_quantize(FAKE + 4, 0, 4, 64, FAKE, FAKE, None) == -2  # alignment
+    assert L.nvfp4_mx_quantize(None, 0, 0, 64, None, None, None) == 0       # empty: no-op
+    # nvfp4_gemm_mx(ac, as, wc, ws, M, N, K, y, dtype, stream)
+    assert L.nvfp4_gemm_mx(FAKE, FAKE, FAKE, FAKE, 32, 32, 128, FAKE, 1, None) == -3  # K % 256
+    assert L.nvfp4_gemm_mx(FAKE, FAKE, FAKE, FAKE, 32, 32, 256, FAKE, 5, None) == -1  # dtype
+    assert L.nvfp4_gemm_mx(FAKE, FAKE, FAKE, FAKE, 32, 32, 256, None, 1, None) == -1  # NULL y
+    assert L.nvfp4_gemm_mx(FAKE, FAKE + 8, FAKE, FAKE, 32, 32, 256, FAKE, 1, None) == -2
+    assert L.nvfp4_gemm_mx(FAKE, FAKE, FAKE, FAKE, 0, 32, 256, None, 1, None) == 0   # empty
+
+
 CFG = nv.KVConfig()
 
 
