@@ -85,6 +85,8 @@ def _declare(L):
     L.orc_e2m1_encode_array.restype = None
     L.orc_e4m3_encode_array.argtypes = [_f32p, _i64, _u8p]
     L.orc_e4m3_encode_array.restype = None
+    L.orc_rht16.argtypes = [_f32p, _i64, _i64, C.c_uint32, _f32p]
+    L.orc_rht16.restype = None
 
 
 def _f32(a):
@@ -174,6 +176,23 @@ def dequantize(codes, scales, s_dec, layout: int = LAYOUT_1D) -> np.ndarray:
 def amax(x) -> np.float32:
     x = _f32(x)
     return np.float32(lib().orc_amax(x.reshape(-1), x.size))
+
+
+def rht16(x, signs: int) -> np.ndarray:
+    """Random Hadamard transform of every 1x16 block of float32 x [R, C]
+    (C % 16 == 0): (1/4) H16 diag(s) x by the fp32 butterfly; bit j of
+    `signs` set flips element j of each block."""
+    x = _f32(x)
+    R, Cc = x.shape
+    out = np.empty_like(x)
+    if x.size:
+        lib().orc_rht16(x.reshape(-1), R, Cc, int(signs) & 0xFFFF, out.reshape(-1))
+    return out
+
+
+def quantize_rht(x, signs: int, search: int = SEARCH_4O6, amax=None):
+    """RHT then 1-D quantize: (codes, scales, s_dec) of rht16(x, signs)."""
+    return quantize(rht16(x, signs), layout=LAYOUT_1D, search=search, amax=amax)
 
 
 # --------------------------------------------------------------------------

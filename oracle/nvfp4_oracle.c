@@ -25,9 +25,10 @@
  *         scaling evaluates 6 and 4 per block and selects the lower-error
  *         encoding; the KV storage formula; FP4 GEMM in place of BF16 GEMM.
  *   [IT]  "LongLive-2.0: Infrastruttura Parallela NVFP4 per Video Lunghi",
- *         sections "Addestramento NVFP4", "Inferenza W4A4 NVFP4"
- *         (micro-block KV scaling with Four Over Six) and "Multi-Shot
- *         Attention Sink".
+ *         sections "Addestramento NVFP4" (a random Hadamard transform is
+ *         applied before quantization on the gradient-sensitive paths),
+ *         "Inferenza W4A4 NVFP4" (micro-block KV scaling with Four Over
+ *         Six) and "Multi-Shot Attention Sink".
  * Where the pages leave a step open the reading taken is marked READING.
  */
 #include "nvfp4_oracle.h"
@@ -473,4 +474,38 @@ void orc_e4m3_encode_array(const float *t, int64_t n, uint8_t *out)
 {
     for (int64_t i = 0; i < n; ++i)
         out[i] = orc_e4m3_encode(t[i]);
+}
+
+/* ------------------------------------------------------------------ */
+/* Random Hadamard transform before quantization                      */
+/* ------------------------------------------------------------------ */
+
+/* [DR] NVFP4 training (RHT stabilises the weight-gradient GEMM), [IT]
+ * Addestramento NVFP4 (an RHT is applied before quantization on the
+ * gradient-sensitive paths).  READING: per 1x16 block along a row,
+ * y = (1/4) * H16 * diag(s) * x with H16 the Sylvester Hadamard matrix,
+ * H16[i][j] = (-1)^popcount(i & j), and s_j = -1 where bit j of `signs` is
+ * set; computed as: sign flips (exact), then the fast Walsh-Hadamard
+ * butterflies with strides 1, 2, 4, 8 -- (a, b) -> (RN(a + b), RN(a - b)) --
+ * then RN(v * 0.25).  The same transform on both GEMM operands along K
+ * leaves the product unchanged ((H S / 4)^T (H S / 4) = I). */
+void orc_rht16(const float *x, int64_t R, int64_t C, uint32_t signs, float *out) {
+    for (int64_t r = 0; r < R; ++r) {
+        for (int64_t b = 0; b < C / 16; ++b) {
+            float v[16];
+            for (int j = 0; j < 16; ++j) {
+                float e = x[r * C + b * 16 + j];
+                v[j] = ((signs >> j) & 1u) ? -e : e;
+            }
+            for (int h = 1; h < 16; h *= 2) {
+                for (int j = 0; j < 16; ++j) {
+                    if (j & h) continue;
+                    float a = v[j], c = v[j + h];
+                    v[j] = a + c;
+                    v[j + h] = a - c;
+                }
+            }
+            for (int j = 0; j < 16; ++j) out[r * C + b * 16 + j] = v[j] * 0.25f;
+        }
+    }
 }
