@@ -18,7 +18,7 @@ recorded around each launch on the launch's own stream, against 8 TB/s.
 bounded sample.  `secondary` carries the W4A4 GEMM (7040x3072x3072, TFLOP/s
 vs the 2.5 PFLOP/s dense fp16/bf16 MFMA peak) and activation quantize lines.
 
-Other workloads (--workload): gemm_attn, ffn, ring64s, quant_act.
+Other workloads (--workload): gemm_attn, ffn, ring64s, quant_act, wgrad.
 """
 from __future__ import annotations
 
@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="kv_chunk",
-                    choices=["kv_chunk", "gemm_attn", "ffn", "ring64s", "quant_act"])
+                    choices=["kv_chunk", "gemm_attn", "ffn", "ring64s", "quant_act", "wgrad"])
     ap.add_argument("--sets", type=int, default=4, help="rotated input/output buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
@@ -342,6 +342,52 @@ def run_ffn(nv, args, dev):
     return {"ms": ms, "wall_ms": wall, "tflops": flops / ms / 1e9, "flops": flops, "kernels": kt}
 
 
+def run_wgrad(nv, args, dev, T=7040, D=3072, signs=0xB7E1, nrows=64):
+    """Weight-gradient GEMM dW = dY^T X (both operands 1-D along the token
+    dimension) with and without the random Hadamard transform: quantize
+    rates, GEMM TFLOP/s, and the relative Frobenius error of dW against the
+    fp64 product of the unquantized operands on `nrows` sampled rows.  The
+    token dimension is padded with zeros to a multiple of 256 (the GEMM's
+    LDS path), which leaves the product unchanged; flops count T."""
+    import numpy as np
+    import torch
+
+    import synth
+
+    X = torch.from_numpy(synth.activations(1021, 0, T, D, 0.005, 30.0)).to(dev).to(torch.bfloat16)
+    dY = torch.from_numpy(synth.activations(1021, 1, T, D, 0.005, 30.0)).to(dev).to(torch.bfloat16)
+    Tp = (T + 255) // 256 * 256
+    Xt = torch.zeros((D, Tp), dtype=torch.bfloat16, device=dev)
+    dYt = torch.zeros_like(Xt)
+    Xt[:, :T] = X.t()
+    dYt[:, :T] = dY.t()
+    ws = torch.empty(nv.quantize_workspace_bytes(D, Tp), dtype=torch.uint8, device=dev)
+    qa = [nv.NVFP4Tensor.empty(D, Tp) for _ in range(2)]
+    qw = [nv.NVFP4Tensor.empty(D, Tp) for _ in range(2)]
+    Y = torch.empty((D, D), dtype=torch.float32, device=dev)
+    out = {}
+    for k, rht in enumerate((False, True)):
+        def quant(i):
+            if rht:
+                nv.quantize_rht(dYt, signs, out=qa[k], workspace=ws)
+                nv.quantize_rht(Xt, signs, out=qw[k], workspace=ws)
+            else:
+                nv.quantize(dYt, out=qa[k], workspace=ws)
+                nv.quantize(Xt, out=qw[k], workspace=ws)
+
+        qms, _ = time_steps(quant, args.steps, args.warmup)
+        gms, _ = time_steps(lambda i: nv.gemm_w4a4(qa[k], qw[k], out=Y), args.steps, args.warmup)
+        rows = np.unique(np.concatenate([[0, D - 1], np.random.default_rng(6).integers(0, D, nrows - 2)]))
+        ref = dY.float().cpu().numpy().astype(np.float64).T[rows] @ X.float().cpu().numpy().astype(np.float64)
+        err = np.linalg.norm(Y.cpu().numpy().astype(np.float64)[rows] - ref) / np.linalg.norm(ref)
+        alg = 2 * (D * T * 2 + D * Tp * 9 // 16 + 4)
+        tag = "rht" if rht else "plain"
+        out[tag] = {"quantize_GB/s": round(alg / qms / 1e6, 1), "quantize_us": round(qms * 1e3, 2),
+                    "gemm_TFLOP/s": round(2.0 * D * D * T / gms / 1e9, 1),
+                    "gemm_us": round(gms * 1e3, 2), "rel_err_vs_fp64_unquantized": round(float(err), 5)}
+    return out
+
+
 def run_ring64s(nv, args, dev):
     """40 chunks; cuts every 10 chunks; per step: gather K_eff(t), store chunk t."""
     import torch
@@ -408,7 +454,7 @@ def main():
 
     if args.workload != "kv_chunk":
         fn = {"gemm_attn": run_gemm_attn, "ffn": run_ffn, "ring64s": run_ring64s,
-              "quant_act": run_quant_act}[args.workload]
+              "quant_act": run_quant_act, "wgrad": run_wgrad}[args.workload]
         r = fn(nv, args, dev)
         r["kernels"] = {k: {"launches": v[0], "mean_ms": v[1]} for k, v in r.get("kernels", {}).items()}
         print(json.dumps({"workload": args.workload, **r}))
@@ -461,6 +507,8 @@ def main():
             "GB/s": round(q["gbs"], 1), "frac_hbm_peak": round(q["gbs"] / HBM_PEAK_GBS, 4),
             "us": round(q["ms"] * 1e3, 2),
             "kernels_us": {k: round(v[1] * 1e3, 2) for k, v in q["kernels"].items()}}
+        w = run_wgrad(nv, argparse.Namespace(steps=10, warmup=3, sets=args.sets), dev)
+        sec["wgrad_3072x3072x7040_1d_operands"] = w
         out["secondary"] = sec
         out["context_copy_GB/s"] = round(copy_gbs(dev), 1)
 

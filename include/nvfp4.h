@@ -124,6 +124,22 @@ int nvfp4_quantize(const void *x, int32_t x_dtype, const nvfp4_tensor *out, int3
                    const float *amax_in, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * nvfp4_quantize with a random Hadamard transform first (DR NVFP4 training:
+ * RHT stabilises the weight-gradient GEMM; IT Addestramento NVFP4: an RHT is
+ * applied before quantization on the gradient-sensitive paths).  Every 1x16
+ * block along a row is replaced by (1/4) H16 diag(s) x -- H16 the Sylvester
+ * Hadamard matrix, s_j = -1 where bit j of `signs` (a 16-bit mask) is set --
+ * computed by the fast Walsh-Hadamard butterflies (strides 1, 2, 4, 8, each
+ * (a, b) -> (RN(a+b), RN(a-b))) and RN(* 0.25); then the tensor amax (of the
+ * transformed values; or *amax_in), scales and 4/6 encode exactly as
+ * nvfp4_quantize.  1-D layout only.  Transforming both operands of a GEMM
+ * along K with the same signs leaves the product unchanged.
+ */
+int nvfp4_quantize_rht(const void *x, int32_t x_dtype, const nvfp4_tensor *out, int32_t search,
+                       uint32_t signs, const float *amax_in, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/*
  * Dequantize `in` into y (device, contiguous [rows, cols], F32 or BF16):
  * y = V(code) * RN(E4M3(scale) * s_dec), rounded to nearest-even for BF16.
  */
@@ -134,7 +150,9 @@ int nvfp4_dequantize(const nvfp4_tensor *in, void *y, int32_t y_dtype, void *str
  * by FP4 GEMMs on NVFP4 weights and activations):
  *   Y[m, n] = RN(RN(s_A * s_W) * sum_k A_hat[m, k] * W_hat[n, k])
  * with A_hat = V * E4M3 scale (exact), likewise W_hat; fp32 accumulation.
- *   a: 1-D layout, [M, K].   w: 2-D layout, [N, K] (rows = output features).
+ *   a: 1-D layout, [M, K].   w: [N, K] (rows = output features), 2-D layout
+ *   for weights, or 1-D for a gradient operand (e.g. the weight-gradient
+ *   GEMM of training, both operands 1-D along the reduction dimension).
  *   y: device, contiguous [M, N] in F32 or BF16 (nearest-even).
  *   amax_out: NULL, or a device fp32 that the call raises to
  *     max(*amax_out, max |y| over the stored y values) -- the tensor amax the

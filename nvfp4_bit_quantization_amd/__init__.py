@@ -70,6 +70,8 @@ _EXPORTS = {
     "nvfp4_quantize": ([C.c_void_p, C.c_int32, C.POINTER(CTensor), C.c_int32, C.c_void_p,
                         C.c_void_p, C.c_size_t, C.c_void_p], C.c_int),
     "nvfp4_dequantize": ([C.POINTER(CTensor), C.c_void_p, C.c_int32, C.c_void_p], C.c_int),
+    "nvfp4_quantize_rht": ([C.c_void_p, C.c_int32, C.POINTER(CTensor), C.c_int32, C.c_uint32,
+                            C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p], C.c_int),
     "nvfp4_gemm_w4a4": ([C.POINTER(CTensor), C.POINTER(CTensor), C.c_void_p, C.c_int32,
                          C.c_void_p, C.c_void_p], C.c_int),
     "nvfp4_mx_quantize": ([C.c_void_p, C.c_int32, C.c_int64, C.c_int64, C.c_void_p,
@@ -188,6 +190,29 @@ def quantize(x: torch.Tensor, layout: int = LAYOUT_1D, search: int = SEARCH_4O6,
     ct = out.c()
     _check(lib().nvfp4_quantize(
         _dev(x, "x"), _DT[x.dtype], C.byref(ct), search,
+        C.c_void_p(amax_in.data_ptr()) if amax_in is not None else None,
+        C.c_void_p(workspace.data_ptr()) if workspace is not None else None,
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(stream)))
+    return out
+
+
+def quantize_rht(x: torch.Tensor, signs: int, search: int = SEARCH_4O6,
+                 amax_in: torch.Tensor | None = None, out: NVFP4Tensor | None = None,
+                 workspace: torch.Tensor | None = None, stream=None) -> NVFP4Tensor:
+    """nvfp4_quantize_rht: random Hadamard transform of every 1x16 block
+    (16-bit sign mask `signs`), then 1-D NVFP4 quantize."""
+    if x.dim() != 2 or x.dtype not in _DT:
+        raise ValueError("quantize_rht expects a 2-D float32 or bfloat16 tensor")
+    rows, cols = x.shape
+    if out is None:
+        out = NVFP4Tensor.empty(rows, cols, LAYOUT_1D, x.device)
+    if workspace is None and amax_in is None:
+        workspace = torch.empty(quantize_workspace_bytes(rows, cols, LAYOUT_1D),
+                                dtype=torch.uint8, device=x.device)
+    ct = out.c()
+    _check(lib().nvfp4_quantize_rht(
+        _dev(x, "x"), _DT[x.dtype], C.byref(ct), search, int(signs),
         C.c_void_p(amax_in.data_ptr()) if amax_in is not None else None,
         C.c_void_p(workspace.data_ptr()) if workspace is not None else None,
         workspace.numel() * workspace.element_size() if workspace is not None else 0,

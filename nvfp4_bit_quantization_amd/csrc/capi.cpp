@@ -214,6 +214,33 @@ int nvfp4_quantize(const void *x, int32_t x_dtype, const nvfp4_tensor *out, int3
     return hip_status(e, "quantize encode launch");
 }
 
+int nvfp4_quantize_rht(const void *x, int32_t x_dtype, const nvfp4_tensor *out, int32_t search,
+                       uint32_t signs, const float *amax_in, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    int st = check_tensor(out, "quantize_rht out");
+    if (st) return st;
+    if (out->layout != NVFP4_LAYOUT_1D)
+        return fail(NVFP4_EINVAL, "quantize_rht: the transform is along rows: 1-D layout only");
+    if (x_dtype != NVFP4_DTYPE_F32 && x_dtype != NVFP4_DTYPE_BF16)
+        return fail(NVFP4_EINVAL, "quantize_rht: bad x dtype %d", x_dtype);
+    if (search != NVFP4_SEARCH_6 && search != NVFP4_SEARCH_4O6)
+        return fail(NVFP4_EINVAL, "quantize_rht: bad search %d", search);
+    if (signs > 0xFFFFu) return fail(NVFP4_EINVAL, "quantize_rht: signs is a 16-bit mask");
+    const int64_t n = out->rows * out->cols;
+    if (n > 0 && !x) return fail(NVFP4_EINVAL, "quantize_rht: NULL x");
+    if (!aligned16(x)) return fail(NVFP4_EALIGN, "quantize_rht: x not 16-byte aligned");
+    if (((uintptr_t)amax_in & 3u)) return fail(NVFP4_EALIGN, "quantize_rht: amax_in misaligned");
+    const size_t need = nvfp4_quantize_workspace_bytes(out->rows, out->cols, out->layout);
+    if (!amax_in && (!workspace || workspace_bytes < need))
+        return fail(NVFP4_ENOSPC, "quantize_rht: workspace %zu < %zu bytes", workspace_bytes,
+                    need);
+    if (!aligned16(workspace)) return fail(NVFP4_EALIGN, "quantize_rht: workspace misaligned");
+    hipError_t e = nvfp4::launch_quantize_rht(x, x_dtype, out->rows, out->cols, search, signs,
+                                              (float *)workspace, amax_in, out->codes,
+                                              out->scales, out->s_dec, (hipStream_t)stream);
+    return hip_status(e, "quantize_rht launch");
+}
+
 int nvfp4_dequantize(const nvfp4_tensor *in, void *y, int32_t y_dtype, void *stream) {
     int st = check_tensor(in, "dequantize in");
     if (st) return st;
@@ -236,8 +263,8 @@ int nvfp4_gemm_w4a4(const nvfp4_tensor *a, const nvfp4_tensor *w, void *y, int32
     if (st) return st;
     if (a->layout != NVFP4_LAYOUT_1D)
         return fail(NVFP4_EINVAL, "gemm: A must use 1-D (1x16) block scaling");
-    if (w->layout != NVFP4_LAYOUT_2D)
-        return fail(NVFP4_EINVAL, "gemm: W must use 2-D (16x16) block scaling");
+    if (w->layout != NVFP4_LAYOUT_2D && w->layout != NVFP4_LAYOUT_1D)
+        return fail(NVFP4_EINVAL, "gemm: bad W layout %d", w->layout);
     if (a->cols != w->cols)
         return fail(NVFP4_ESHAPE, "gemm: K mismatch (A has %lld, W has %lld)",
                     (long long)a->cols, (long long)w->cols);
@@ -247,8 +274,8 @@ int nvfp4_gemm_w4a4(const nvfp4_tensor *a, const nvfp4_tensor *w, void *y, int32
     if (!aligned16(y)) return fail(NVFP4_EALIGN, "gemm: y not 16-byte aligned");
     if (((uintptr_t)amax_out & 3u)) return fail(NVFP4_EALIGN, "gemm: amax_out misaligned");
     hipError_t e = nvfp4::launch_gemm_w4a4(a->codes, a->scales, a->s_dec, w->codes, w->scales,
-                                           w->s_dec, a->rows, w->rows, a->cols, y, y_dtype,
-                                           amax_out, (hipStream_t)stream);
+                                           w->s_dec, a->rows, w->rows, a->cols, w->layout, y,
+                                           y_dtype, amax_out, (hipStream_t)stream);
     return hip_status(e, "gemm launch");
 }
 

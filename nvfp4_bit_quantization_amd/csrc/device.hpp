@@ -117,6 +117,30 @@ __device__ __forceinline__ float div6_rn(float a) {
 }
 
 // ---------------------------------------------------------------------------
+// random Hadamard transform of one 1x16 block held by one lane
+// ---------------------------------------------------------------------------
+
+// (1/4) H16 diag(s) v: bit j of `signs` flips element j (exact), then the
+// fast Walsh-Hadamard butterflies with strides 1, 2, 4, 8 -- (a, b) ->
+// (RN(a + b), RN(a - b)) -- then RN(v * 0.25).  H16 is the Sylvester
+// Hadamard matrix (entry (i, j) = (-1)^popcount(i & j)).
+__device__ __forceinline__ void rht16(float (&v)[16], uint32_t signs) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = ((signs >> j) & 1u) ? -v[j] : v[j];
+#pragma unroll
+    for (int h = 1; h < 16; h *= 2)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (j & h) continue;
+            const float a = v[j], c = v[j + h];
+            v[j] = a + c;
+            v[j + h] = a - c;
+        }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = v[j] * 0.25f;
+}
+
+// ---------------------------------------------------------------------------
 // one 1x16 block held by one lane: the Four-Over-Six encoder
 // ---------------------------------------------------------------------------
 

@@ -56,12 +56,13 @@ constexpr int NSUB = BK / 16;               // MFMA substeps per step
 constexpr int kXcds = 8;
 
 // LDS stage layout (bytes): A codes (BM / 8 blocks of 8 rows x 128 bytes),
-// W codes, A scales (16 bytes per row), W scales (16 bytes per 16-row group).
+// W codes, A scales (16 bytes per row), W scales (16 bytes per row for 1-D
+// W, per 16-row group for 2-D W).
 constexpr int kAOff = 0;
 constexpr int kBOff = kAOff + BM * 128;
 constexpr int kASOff = kBOff + BN * 128;
 constexpr int kBSOff = kASOff + BM * 16;
-constexpr int kStage = kBSOff + (BN / 16) * 16 + 64;  // 61696 bytes
+constexpr int kStage = kBSOff + BN * 16;  // 64512 bytes
 constexpr int kLdsBytes = 2 * kStage;
 static_assert(kStage % 256 == 0, "stage alignment");
 
@@ -186,7 +187,7 @@ struct StageSrc {
     uint32_t a[BM / 32], w[BN / 32], asr, wsr;
 };
 
-template <bool SCALES>
+template <bool SCALES, bool W2D>
 __device__ __forceinline__ void stage_src(StageSrc &q, const GemmArgs &g, int64_t m0, int64_t n0,
                                           int wave, int lane) {
     const int64_t kbytes = g.K >> 1, KB = g.K >> 4;
@@ -198,7 +199,8 @@ __device__ __forceinline__ void stage_src(StageSrc &q, const GemmArgs &g, int64_
         q.as = __builtin_amdgcn_make_buffer_rsrc((void *)g.a_scales, (short)0, (int)(g.M * KB),
                                                  kBufferWord3);
         q.ws = __builtin_amdgcn_make_buffer_rsrc((void *)g.w_scales, (short)0,
-                                                 (int)((g.N >> 4) * KB), kBufferWord3);
+                                                 (int)((W2D ? g.N >> 4 : g.N) * KB),
+                                                 kBufferWord3);
     }
     const int rib = lane >> 3, gcol = (lane & 7) ^ rib;
 #pragma unroll
@@ -215,13 +217,18 @@ __device__ __forceinline__ void stage_src(StageSrc &q, const GemmArgs &g, int64_
     }
     const int64_t ar0 = m0 + wave * 64 + lane;
     q.asr = (uint32_t)((ar0 < g.M ? ar0 : g.M - 1) * KB);
-    const int64_t gr0 = (n0 >> 4) + lane, glast = (g.N >> 4) - 1;
-    q.wsr = (uint32_t)((gr0 < glast ? gr0 : glast) * KB);
+    if (W2D) {
+        const int64_t gr0 = (n0 >> 4) + lane, glast = (g.N >> 4) - 1;
+        q.wsr = (uint32_t)((gr0 < glast ? gr0 : glast) * KB);
+    } else {
+        const int64_t wr0 = n0 + (wave < BN / 64 ? wave : 0) * 64 + lane;
+        q.wsr = (uint32_t)((wr0 < g.N ? wr0 : g.N - 1) * KB);
+    }
 }
 
 // Issue this wave's direct-to-LDS loads of K step kt into `stage` (codes,
 // and with SCALES the NVFP4 block scales).
-template <bool SCALES>
+template <bool SCALES, bool W2D>
 __device__ __forceinline__ void stage_load(const StageSrc &q, uint8_t *stage, int64_t kt, int wave,
                                            int lane) {
     const uint32_t kc = (uint32_t)kt * 128, ks = (uint32_t)kt * 16;
@@ -236,15 +243,20 @@ __device__ __forceinline__ void stage_load(const StageSrc &q, uint8_t *stage, in
     if (!SCALES) return;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(q.as, (lvoid)(stage + kASOff + wave * 1024), 16,
                                              q.asr, ks, 0, 0);
-    if (wave == 0 && lane < BN / 16)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(q.ws, (lvoid)(stage + kBSOff), 16, q.wsr, ks, 0,
-                                                 0);
+    if (W2D) {
+        if (wave == 0 && lane < BN / 16)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(q.ws, (lvoid)(stage + kBSOff), 16, q.wsr, ks,
+                                                     0, 0);
+    } else if (wave < BN / 64) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(q.ws, (lvoid)(stage + kBSOff + wave * 1024), 16,
+                                                 q.wsr, ks, 0, 0);
+    }
 }
 
 // The wave's fragments of one K step from LDS: lane (r, h) reads, for each
 // fragment row R, the 16-byte columns 4h .. 4h + 3 (un-swizzled) and the 8
 // scale bytes of its half.
-template <bool SCALES>
+template <bool SCALES, bool W2D>
 __device__ __forceinline__ void stage_read(Frag (&A)[FM], Frag (&B)[FN], const uint8_t *stage,
                                            int wm, int wn, int r, int h) {
     const int rib = r & 7;
@@ -253,8 +265,10 @@ __device__ __forceinline__ void stage_read(Frag (&A)[FM], Frag (&B)[FN], const u
         for (int i = 0; i < FM; ++i)
             A[i].sc = *(const u32x2 *)(stage + kASOff + (wm * WM + i * 32 + r) * 16 + h * 8);
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-            B[j].sc = *(const u32x2 *)(stage + kBSOff + ((wn * WN + j * 32 + r) >> 4) * 16 + h * 8);
+        for (int j = 0; j < FN; ++j) {
+            const int R = wn * WN + j * 32 + r;
+            B[j].sc = *(const u32x2 *)(stage + kBSOff + (W2D ? R >> 4 : R) * 16 + h * 8);
+        }
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -274,7 +288,7 @@ __device__ __forceinline__ void step_all(f32x16 (&acc)[FM][FN], const Frag (&A)[
     (substep<S>(acc, A, B), ...);
 }
 
-template <bool OUT_BF16, bool KFAST>
+template <bool OUT_BF16, bool KFAST, bool W2D>
 __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float *__restrict__ a_sdec,
                                                         const float *__restrict__ w_sdec,
                                                         void *__restrict__ yv,
@@ -311,8 +325,8 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
     if (KFAST) {
         extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
         StageSrc src;
-        stage_src<true>(src, g, m0, n0, wave, lane);
-        stage_load<true>(src, lds, 0, wave, lane);
+        stage_src<true, W2D>(src, g, m0, n0, wave, lane);
+        stage_load<true, W2D>(src, lds, 0, wave, lane);
         // Each iteration: this wave's loads of step kt have landed; after the
         // barrier so have everyone's, and nobody still reads the stage that
         // the loads of step kt + 1 overwrite.  The last iteration reloads its
@@ -323,8 +337,8 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __syncthreads();
                 const int64_t kn = kt + 1 < nk ? kt + 1 : kt;
-                stage_read<true>(A, B, lds + (kt & 1) * kStage, wm, wn, r, h);
-                stage_load<true>(src, lds + ((kt + 1) & 1) * kStage, kn, wave, lane);
+                stage_read<true, W2D>(A, B, lds + (kt & 1) * kStage, wm, wn, r, h);
+                stage_load<true, W2D>(src, lds + ((kt + 1) & 1) * kStage, kn, wave, lane);
                 step_all(acc, A, B, std::make_integer_sequence<int, NSUB>{});
             }
         } else {
@@ -332,7 +346,7 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __syncthreads();
                 const int64_t kn = kt + 1 < nk ? kt + 1 : kt;
-                stage_load<true>(src, lds + ((kt + 1) & 1) * kStage, kn, wave, lane);
+                stage_load<true, W2D>(src, lds + ((kt + 1) & 1) * kStage, kn, wave, lane);
             }
         }
         // no load into LDS is still in flight when the wave leaves
@@ -344,7 +358,7 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
             pa[i] = frag_ptr(g.a_codes, g.a_scales, mw + i * 32 + r, M, K, false, h);
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-            pb[j] = frag_ptr(g.w_codes, g.w_scales, nw + j * 32 + r, N, K, true, h);
+            pb[j] = frag_ptr(g.w_codes, g.w_scales, nw + j * 32 + r, N, K, W2D, h);
         for (int64_t kt = 0; kt < nk; ++kt) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) load_frag_general(A[i], pa[i], kt, K, h);
@@ -387,8 +401,8 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
 
 hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_sdec,
                             const uint8_t *w_codes, const uint8_t *w_scales,
-                            const float *w_sdec, int64_t M, int64_t N, int64_t K, void *y,
-                            int ydtype, float *amax_out, hipStream_t s) {
+                            const float *w_sdec, int64_t M, int64_t N, int64_t K, int w_layout,
+                            void *y, int ydtype, float *amax_out, hipStream_t s) {
     if (M == 0 || N == 0) return hipSuccess;
     const int64_t ntiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const dim3 grid((unsigned)ntiles);
@@ -398,8 +412,10 @@ hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, con
                       N * (K / 2) < ((int64_t)1 << 31);
     static bool attr_set = false;
     if (!attr_set) {
-        const void *fns[2] = {(const void *)gemm_w4a4_kernel<true, true>,
-                              (const void *)gemm_w4a4_kernel<false, true>};
+        const void *fns[4] = {(const void *)gemm_w4a4_kernel<true, true, true>,
+                              (const void *)gemm_w4a4_kernel<false, true, true>,
+                              (const void *)gemm_w4a4_kernel<true, true, false>,
+                              (const void *)gemm_w4a4_kernel<false, true, false>};
         for (const void *f : fns) {
             hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
                                                kLdsBytes);
@@ -407,20 +423,28 @@ hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, con
         }
         attr_set = true;
     }
-#define NVFP4_GEMM(BF, KF)                                                                  \
-    NVFP4_LAUNCH("gemm_w4a4", (gemm_w4a4_kernel<BF, KF>), grid, dim3(256), KF ? kLdsBytes : 0, \
-                 s, g, a_sdec, w_sdec, y, amax_out)
+#define NVFP4_GEMM(BF, KF, W2)                                                                \
+    NVFP4_LAUNCH("gemm_w4a4", (gemm_w4a4_kernel<BF, KF, W2>), grid, dim3(256),               \
+                 KF ? kLdsBytes : 0, s, g, a_sdec, w_sdec, y, amax_out)
+#define NVFP4_GEMM_K(BF, W2)        \
+    if (fast)                       \
+        NVFP4_GEMM(BF, true, W2);   \
+    else                            \
+        NVFP4_GEMM(BF, false, W2);
     if (ydtype == kBF16) {
-        if (fast)
-            NVFP4_GEMM(true, true);
-        else
-            NVFP4_GEMM(true, false);
+        if (w_layout) {
+            NVFP4_GEMM_K(true, true)
+        } else {
+            NVFP4_GEMM_K(true, false)
+        }
     } else {
-        if (fast)
-            NVFP4_GEMM(false, true);
-        else
-            NVFP4_GEMM(false, false);
+        if (w_layout) {
+            NVFP4_GEMM_K(false, true)
+        } else {
+            NVFP4_GEMM_K(false, false)
+        }
     }
+#undef NVFP4_GEMM_K
 #undef NVFP4_GEMM
     return hipGetLastError();
 }
@@ -508,8 +532,8 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs g, void *__restri
     Frag A[FM], B[FN];
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     StageSrc src;
-    stage_src<false>(src, g, m0, n0, wave, lane);
-    stage_load<false>(src, lds, 0, wave, lane);
+    stage_src<false, true>(src, g, m0, n0, wave, lane);
+    stage_load<false, true>(src, lds, 0, wave, lane);
     if (active) {
         for (int64_t kt = 0; kt < nk; ++kt) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -519,8 +543,8 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs g, void *__restri
             for (int i = 0; i < FM; ++i) A[i].sc.x = *(const uint32_t *)(sa[i] + kt * 8);
 #pragma unroll
             for (int j = 0; j < FN; ++j) B[j].sc.x = *(const uint32_t *)(sb[j] + kt * 8);
-            stage_read<false>(A, B, lds + (kt & 1) * kStage, wm, wn, r, h);
-            stage_load<false>(src, lds + ((kt + 1) & 1) * kStage, kn, wave, lane);
+            stage_read<false, true>(A, B, lds + (kt & 1) * kStage, wm, wn, r, h);
+            stage_load<false, true>(src, lds + ((kt + 1) & 1) * kStage, kn, wave, lane);
             mx_step(acc, A, B, std::make_integer_sequence<int, 4>{});
         }
     } else {
@@ -528,7 +552,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(GemmArgs g, void *__restri
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             const int64_t kn = kt + 1 < nk ? kt + 1 : kt;
-            stage_load<false>(src, lds + ((kt + 1) & 1) * kStage, kn, wave, lane);
+            stage_load<false, true>(src, lds + ((kt + 1) & 1) * kStage, kn, wave, lane);
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

@@ -91,11 +91,14 @@ hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
 // ---- gemm.hip
 hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_sdec,
                             const uint8_t *w_codes, const uint8_t *w_scales,
-                            const float *w_sdec, int64_t M, int64_t N, int64_t K, void *y,
-                            int ydtype, float *amax_out, hipStream_t s);
+                            const float *w_sdec, int64_t M, int64_t N, int64_t K, int w_layout,
+                            void *y, int ydtype, float *amax_out, hipStream_t s);
 hipError_t launch_gemm_mx(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *w_codes,
                           const uint8_t *w_scales, int64_t M, int64_t N, int64_t K, void *y,
                           int ydtype, hipStream_t s);
+hipError_t launch_quantize_rht(const void *x, int dtype, int64_t rows, int64_t cols, int search,
+                               uint32_t signs, float *partials, const float *amax_in,
+                               uint8_t *codes, uint8_t *scales, float *s_dec, hipStream_t s);
 hipError_t launch_mx_quantize(const void *x, int xdtype, int64_t rows, int64_t cols,
                               uint8_t *codes, uint8_t *scales, hipStream_t s);
 

@@ -53,6 +53,40 @@ __global__ __launch_bounds__(256) void amax_kernel(const T *__restrict__ x, int6
     }
 }
 
+// Amax partials of the random-Hadamard-transformed tensor: one lane per 1x16
+// block, two blocks in flight.
+template <typename T>
+__global__ __launch_bounds__(256) void amax_rht_kernel(const T *__restrict__ x, int64_t nblk,
+                                                       uint32_t signs,
+                                                       float *__restrict__ partials) {
+    typedef typename Raw16Of<T>::type Raw;
+    float m = 0.0f;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += 2 * stride) {
+        const int64_t b2 = b + stride;
+        Raw r0, r1;
+        load_raw16(x + b * 16, r0);
+        if (b2 < nblk) load_raw16(x + b2 * 16, r1);
+        float v[16];
+        unpack16(r0, v);
+        rht16(v, signs);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+        if (b2 < nblk) {
+            unpack16(r1, v);
+            rht16(v, signs);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+        }
+    }
+    m = wave_max(m);
+    __shared__ float red[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) partials[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
 // Reduce `np` partial maxima (or take *amax_in), derive the tensor scales and
 // build the per-scale-code table (S, r): S = RN(sigma * s_dec), r = RN(1 / S)
 // (0 when S == 0).  Called by every workgroup of the encode kernels.
@@ -140,11 +174,12 @@ __device__ __forceinline__ void encode_half_block(const float (&x)[8], float s_e
 // 1-D encode: one lane per 1x16 block, two blocks in flight per lane
 // ---------------------------------------------------------------------------
 
-template <typename T, bool FOUR_OVER_SIX>
+// With RHT every block is first transformed by rht16 (signs).
+template <typename T, bool FOUR_OVER_SIX, bool RHT>
 __global__ __launch_bounds__(256) void encode1d_kernel(
     const T *__restrict__ x, int64_t nblk, const float *__restrict__ partials, int np,
     const float *__restrict__ amax_in, uint2 *__restrict__ codes, uint8_t *__restrict__ scales,
-    float *__restrict__ s_dec_out) {
+    float *__restrict__ s_dec_out, uint32_t signs) {
     __shared__ f32x2 lut[128];
     float s_enc;
     encode_prologue(partials, np, amax_in, s_dec_out, lut, s_enc);
@@ -158,11 +193,13 @@ __global__ __launch_bounds__(256) void encode1d_kernel(
         float v[16];
         uint32_t lo, hi, sc;
         unpack16(r0, v);
+        if (RHT) rht16(v, signs);
         encode_block16<FOUR_OVER_SIX>(v, s_enc, lut, lo, hi, sc);
         codes[b] = make_uint2(lo, hi);
         scales[b] = (uint8_t)sc;
         if (b2 < nblk) {
             unpack16(r1, v);
+            if (RHT) rht16(v, signs);
             encode_block16<FOUR_OVER_SIX>(v, s_enc, lut, lo, hi, sc);
             codes[b2] = make_uint2(lo, hi);
             scales[b2] = (uint8_t)sc;
@@ -293,8 +330,8 @@ hipError_t launch_encode(const void *x, int dtype, int64_t rows, int64_t cols, i
         const int g = grid_for(nblk, 256, kStreamGrid);
         uint2 *c64 = (uint2 *)codes;
 #define L1(T, F)                                                                          \
-    NVFP4_LAUNCH("encode1d", (encode1d_kernel<T, F>), dim3(g), dim3(256), 0, s, (const T *)x, \
-                 nblk, partials, np, amax_in, c64, scales, s_dec)
+    NVFP4_LAUNCH("encode1d", (encode1d_kernel<T, F, false>), dim3(g), dim3(256), 0, s,        \
+                 (const T *)x, nblk, partials, np, amax_in, c64, scales, s_dec, 0u)
         if (dtype == kF32) {
             if (f46) L1(float, true); else L1(float, false);
         } else {
@@ -314,6 +351,38 @@ hipError_t launch_encode(const void *x, int dtype, int64_t rows, int64_t cols, i
         }
 #undef L2
     }
+    return hipGetLastError();
+}
+
+int amax_rht_partials_for(int64_t n) { return grid_for(n / 16, 256 * 2, kMaxPartials); }
+
+hipError_t launch_quantize_rht(const void *x, int dtype, int64_t rows, int64_t cols, int search,
+                               uint32_t signs, float *partials, const float *amax_in,
+                               uint8_t *codes, uint8_t *scales, float *s_dec, hipStream_t s) {
+    const int64_t nblk = rows * cols / 16;
+    int np = 0;
+    if (!amax_in) {
+        np = amax_rht_partials_for(rows * cols);
+        if (dtype == kF32)
+            NVFP4_LAUNCH("amax_rht", amax_rht_kernel<float>, dim3(np), dim3(256), 0, s,
+                         (const float *)x, nblk, signs, partials);
+        else
+            NVFP4_LAUNCH("amax_rht", amax_rht_kernel<uint16_t>, dim3(np), dim3(256), 0, s,
+                         (const uint16_t *)x, nblk, signs, partials);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int g = grid_for(nblk, 256, kStreamGrid);
+    uint2 *c64 = (uint2 *)codes;
+#define LR(T, F)                                                                            \
+    NVFP4_LAUNCH("encode1d_rht", (encode1d_kernel<T, F, true>), dim3(g), dim3(256), 0, s,   \
+                 (const T *)x, nblk, partials, np, amax_in, c64, scales, s_dec, signs)
+    if (dtype == kF32) {
+        if (search == 1) LR(float, true); else LR(float, false);
+    } else {
+        if (search == 1) LR(uint16_t, true); else LR(uint16_t, false);
+    }
+#undef LR
     return hipGetLastError();
 }
 

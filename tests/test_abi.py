@@ -79,12 +79,23 @@ def test_dequantize_and_gemm_validation(L):
     assert L.nvfp4_dequantize(C.byref(t), FAKE + 2, 1, None) == -2
     a, w = tensor(64, 64), tensor(32, 64, nv.LAYOUT_2D)
     assert L.nvfp4_gemm_w4a4(C.byref(w), C.byref(w), FAKE, 1, None, None) == -1  # A must be 1-D
-    assert L.nvfp4_gemm_w4a4(C.byref(a), C.byref(a), FAKE, 1, None, None) == -1  # W must be 2-D
+    w7 = tensor(32, 64, 7)
+    assert L.nvfp4_gemm_w4a4(C.byref(a), C.byref(w7), FAKE, 1, None, None) == -1  # bad W layout
     w2 = tensor(32, 128, nv.LAYOUT_2D)
     assert L.nvfp4_gemm_w4a4(C.byref(a), C.byref(w2), FAKE, 1, None, None) == -3
     assert L.nvfp4_gemm_w4a4(C.byref(a), C.byref(w), FAKE, 4, None, None) == -1
     assert L.nvfp4_gemm_w4a4(C.byref(a), C.byref(w), None, 1, None, None) == -1
     assert L.nvfp4_gemm_w4a4(C.byref(a), C.byref(w), FAKE, 1, FAKE + 2, None) == -2  # amax_out
+
+
+def test_quantize_rht_validation(L):
+    # nvfp4_quantize_rht(x, dtype, out, search, signs, amax_in, ws, ws_bytes, stream)
+    t1, t2 = tensor(32, 64), tensor(32, 64, nv.LAYOUT_2D)
+    assert L.nvfp4_quantize_rht(FAKE, 1, C.byref(t2), 1, 0x1234, None, FAKE, 1 << 20, None) == -1
+    assert L.nvfp4_quantize_rht(FAKE, 1, C.byref(t1), 1, 0x10000, None, FAKE, 1 << 20, None) == -1
+    assert L.nvfp4_quantize_rht(FAKE, 1, C.byref(t1), 3, 0x1234, None, FAKE, 1 << 20, None) == -1
+    assert L.nvfp4_quantize_rht(FAKE, 1, C.byref(t1), 1, 0x1234, None, FAKE, 4, None) == -4
+    assert L.nvfp4_quantize_rht(FAKE + 8, 1, C.byref(t1), 1, 0x1234, None, FAKE, 1 << 20, None) == -2
 
 
 def test_mx_reference_validation(L):
