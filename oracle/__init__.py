@@ -87,6 +87,9 @@ def _declare(L):
     L.orc_e4m3_encode_array.restype = None
     L.orc_rht16.argtypes = [_f32p, _i64, _i64, C.c_uint32, _f32p]
     L.orc_rht16.restype = None
+    L.orc_lora_ref.argtypes = [_f32p, _f32p, _f32p, _i64, _i64, _i64, _i64, C.c_float,
+                               C.c_void_p, _i64, _f64p, C.c_void_p, C.c_void_p]
+    L.orc_lora_ref.restype = C.c_int
 
 
 def _f32(a):
@@ -305,3 +308,27 @@ def gemm_ref(a_codes, a_scales, a_sdec, w_codes, w_scales, w_sdec, w_layout: int
     if rc != 0:
         raise RuntimeError("orc_gemm_ref failed")
     return y, s
+
+
+def lora_ref(x, a, b, scale: float, rows=None):
+    """LoRA branch of the frozen-backbone linear layer: (alpha/r) XA B^T with
+    XA = bf16(x A^T).  x [M, K], a [r, K], b [N, r] float32 (bf16 values).
+    Returns (y fp64 [len(rows) or M, N], abs-sum bound term, XA float32 [M, r])."""
+    x, a, b = _f32(x), _f32(a), _f32(b)
+    M, K = x.shape
+    r = a.shape[0]
+    N = b.shape[0]
+    if a.shape[1] != K or b.shape[1] != r:
+        raise ValueError("lora_ref: shapes do not chain")
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, np.int64)
+    nr = len(rows) if rows is not None else M
+    y = np.empty((nr, N), np.float64)
+    s = np.empty((nr, N), np.float64)
+    xa = np.zeros((M, r), np.float32)
+    rc = lib().orc_lora_ref(x.reshape(-1), a.reshape(-1), b.reshape(-1), M, K, N, r,
+                            float(scale), rows.ctypes.data if rows is not None else None, nr,
+                            y.reshape(-1), s.ctypes.data, xa.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("orc_lora_ref failed")
+    return y, s, xa

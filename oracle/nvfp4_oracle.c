@@ -509,3 +509,66 @@ void orc_rht16(const float *x, int64_t R, int64_t C, uint32_t signs, float *out)
         }
     }
 }
+
+/* ------------------------------------------------------------------ */
+/* LoRA adapter on the frozen NVFP4 backbone                          */
+/* ------------------------------------------------------------------ */
+
+/* [DR] Few-step distillation: the trainable model is the frozen quantized
+ * backbone plus LoRA adapters, W ~ Dequant(Q_search(W_0)) + dW with
+ * dW = (alpha / r) B A; [IT] the distillation trains only the LoRA adapters
+ * on the frozen quantized backbone.  Forward through dW for activations x:
+ * x dW^T = (alpha / r) (x A^T) B^T.  READING: the adapter branch runs in
+ * bf16 like the activations: the down projection x A^T is an fp32 result
+ * stored as bf16, XA = bf16(fp32(x A^T)) (each nearest-even; fp32 of the
+ * exact dot product here), then (alpha / r) * XA B^T, added to the W4A4
+ * product.
+ * x [M, K], A [r, K], B [N, r] row-major float32 (bf16 values); `scale` is
+ * alpha / r as one float.  y[i, n] and abs_sum[i, n] (optional) for the rows
+ * `rows` (or all M); xa [M, r] (optional) receives XA as float. */
+int orc_lora_ref(const float *x, const float *a, const float *b, int64_t M, int64_t K,
+                 int64_t N, int64_t r, float scale, const int64_t *rows, int64_t nrows,
+                 double *y, double *abs_sum, float *xa)
+{
+    int64_t nr = rows ? nrows : M;
+    double *xr = (double *)malloc((size_t)(r > 0 ? r : 1) * sizeof(double));
+    if (!xr)
+        return -2;
+    for (int64_t i = 0; i < nr; ++i) {
+        int64_t m = rows ? rows[i] : i;
+        if (m < 0 || m >= M) {
+            free(xr);
+            return -1;
+        }
+        for (int64_t j = 0; j < r; ++j) {
+            double d = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                d += (double)x[m * K + k] * (double)a[j * K + k];
+            /* the double sum of products of bf16 values is exact unless the
+             * exponents differ widely; round it to fp32, then to bf16 */
+            float f = (float)d;
+            uint16_t hb = orc_bf16_rne(f);
+            union {
+                uint32_t u;
+                float f;
+            } cv;
+            cv.u = (uint32_t)hb << 16;
+            xr[j] = (double)cv.f;
+            if (xa)
+                xa[m * r + j] = cv.f;
+        }
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0, aacc = 0.0;
+            for (int64_t j = 0; j < r; ++j) {
+                double p = xr[j] * (double)b[n * r + j];
+                acc += p;
+                aacc += fabs(p);
+            }
+            y[i * N + n] = (double)scale * acc;
+            if (abs_sum)
+                abs_sum[i * N + n] = fabs((double)scale) * aacc;
+        }
+    }
+    free(xr);
+    return 0;
+}

@@ -43,6 +43,9 @@ int orc_gemm_ref(const uint8_t *a_codes, const uint8_t *a_scales, float a_sdec, 
                  double *abs_sum);
 void orc_e2m1_encode_array(const float *y, int64_t n, uint8_t *out);
 void orc_rht16(const float *x, int64_t R, int64_t C, uint32_t signs, float *out);
+int orc_lora_ref(const float *x, const float *a, const float *b, int64_t M, int64_t K,
+                 int64_t N, int64_t r, float scale, const int64_t *rows, int64_t nrows,
+                 double *y, double *abs_sum, float *xa);
 void orc_e4m3_encode_array(const float *t, int64_t n, uint8_t *out);
 
 #endif
