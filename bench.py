@@ -18,7 +18,7 @@ recorded around each launch on the launch's own stream, against 8 TB/s.
 bounded sample.  `secondary` carries the W4A4 GEMM (7040x3072x3072, TFLOP/s
 vs the 2.5 PFLOP/s dense fp16/bf16 MFMA peak) and activation quantize lines.
 
-Other workloads (--workload): gemm_attn, ffn, ring64s, quant_act, wgrad.
+Other workloads (--workload): gemm_attn, ffn, ring64s, quant_act, wgrad, lora.
 """
 from __future__ import annotations
 
@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="kv_chunk",
-                    choices=["kv_chunk", "gemm_attn", "ffn", "ring64s", "quant_act", "wgrad"])
+                    choices=["kv_chunk", "gemm_attn", "ffn", "ring64s", "quant_act", "wgrad",
+                             "lora"])
     ap.add_argument("--sets", type=int, default=4, help="rotated input/output buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
@@ -342,6 +343,33 @@ def run_ffn(nv, args, dev):
     return {"ms": ms, "wall_ms": wall, "tflops": flops / ms / 1e9, "flops": flops, "kernels": kt}
 
 
+def run_lora(nv, args, dev, M=7040, N=3072, K=3072, r=32, alpha=32.0):
+    """W4A4 layer with a LoRA adapter on the frozen backbone: lora_down
+    (XA = bf16(X A^T)) plus the GEMM with the adapter in its epilogue, timed
+    against the plain W4A4 GEMM on the same operands."""
+    import torch
+
+    import synth
+
+    X, qa, qw, Y = setup_gemm(nv, dev, M, N, K)
+    A = torch.from_numpy(synth.weights(1041, 2, r, K, 0.05)).to(dev).to(torch.bfloat16)
+    B = torch.from_numpy(synth.weights(1041, 3, N, r, 0.05)).to(dev).to(torch.bfloat16)
+    XA = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        nv.lora_down(X, A, out=XA)
+        nv.gemm_w4a4_lora(qa, qw, XA, B, alpha / r, out=Y)
+
+    ms, _ = time_steps(step, args.steps, args.warmup)
+    kt = kernel_times(nv, step, max(5, args.steps // 5), 0)
+    base, _ = time_steps(lambda i: nv.gemm_w4a4(qa, qw, out=Y), args.steps, args.warmup)
+    flops = 2.0 * M * N * K
+    return {"rank": r, "ms": ms, "plain_gemm_ms": base,
+            "overhead_vs_plain": ms / base - 1.0,
+            "lora_down_us": kt["lora_down"][1] * 1e3, "gemm_lora_us": kt["gemm_w4a4_lora"][1] * 1e3,
+            "tflops_backbone": flops / ms / 1e9}
+
+
 def run_wgrad(nv, args, dev, T=7040, D=3072, signs=0xB7E1, nrows=64):
     """Weight-gradient GEMM dW = dY^T X (both operands 1-D along the token
     dimension) with and without the random Hadamard transform: quantize
@@ -454,7 +482,7 @@ def main():
 
     if args.workload != "kv_chunk":
         fn = {"gemm_attn": run_gemm_attn, "ffn": run_ffn, "ring64s": run_ring64s,
-              "quant_act": run_quant_act, "wgrad": run_wgrad}[args.workload]
+              "quant_act": run_quant_act, "wgrad": run_wgrad, "lora": run_lora}[args.workload]
         r = fn(nv, args, dev)
         r["kernels"] = {k: {"launches": v[0], "mean_ms": v[1]} for k, v in r.get("kernels", {}).items()}
         print(json.dumps({"workload": args.workload, **r}))
@@ -509,6 +537,9 @@ def main():
             "kernels_us": {k: round(v[1] * 1e3, 2) for k, v in q["kernels"].items()}}
         w = run_wgrad(nv, argparse.Namespace(steps=10, warmup=3, sets=args.sets), dev)
         sec["wgrad_3072x3072x7040_1d_operands"] = w
+        lo = run_lora(nv, argparse.Namespace(steps=20, warmup=5, sets=args.sets), dev)
+        sec["lora_r32_7040x3072x3072"] = {k: (round(v, 4) if isinstance(v, float) else v)
+                                          for k, v in lo.items()}
         out["secondary"] = sec
         out["context_copy_GB/s"] = round(copy_gbs(dev), 1)
 

@@ -165,6 +165,27 @@ int nvfp4_dequantize(const nvfp4_tensor *in, void *y, int32_t y_dtype, void *str
 int nvfp4_gemm_w4a4(const nvfp4_tensor *a, const nvfp4_tensor *w, void *y, int32_t y_dtype,
                     float *amax_out, void *stream);
 
+/*
+ * LoRA on the frozen NVFP4 backbone (DR few-step distillation: the model is
+ * the frozen quantized backbone plus LoRA adapters, W ~ Dequant(Q_search(W_0))
+ * + (alpha/r) B A; IT: only the LoRA adapters are trained on the frozen
+ * quantized backbone).  The layer's output is the W4A4 product plus the
+ * adapter branch (alpha/r) (x A^T) B^T, the branch in bf16:
+ *
+ * nvfp4_lora_down: xa[M, r] = bf16(x A^T), fp32 accumulation, nearest-even;
+ *   x [M, K] and a [r, K] bf16, row-major device memory; r in {16, 32, 64,
+ *   128}; K % 32 == 0.
+ * nvfp4_gemm_w4a4_lora: as nvfp4_gemm_w4a4, with
+ *   y = fma(lora_scale, sum_j xa[m, j] b[n, j], RN(RN(s_A s_W) acc))
+ *   (the branch on the bf16 MFMA, fp32 accumulation); xa [M, r] and
+ *   b [N, r] bf16, r as above; lora_scale = alpha / r.
+ */
+int nvfp4_lora_down(const void *x_bf16, const void *a_bf16, int64_t M, int64_t K, int64_t r,
+                    void *xa_bf16, void *stream);
+int nvfp4_gemm_w4a4_lora(const nvfp4_tensor *a, const nvfp4_tensor *w, const void *xa_bf16,
+                         const void *b_bf16, int64_t r, float lora_scale, void *y,
+                         int32_t y_dtype, float *amax_out, void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* MXFP4 speed reference (not part of the method)                            */
 /* ------------------------------------------------------------------------ */

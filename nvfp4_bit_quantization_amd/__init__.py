@@ -74,6 +74,11 @@ _EXPORTS = {
                             C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p], C.c_int),
     "nvfp4_gemm_w4a4": ([C.POINTER(CTensor), C.POINTER(CTensor), C.c_void_p, C.c_int32,
                          C.c_void_p, C.c_void_p], C.c_int),
+    "nvfp4_lora_down": ([C.c_void_p, C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p,
+                         C.c_void_p], C.c_int),
+    "nvfp4_gemm_w4a4_lora": ([C.POINTER(CTensor), C.POINTER(CTensor), C.c_void_p, C.c_void_p,
+                              C.c_int64, C.c_float, C.c_void_p, C.c_int32, C.c_void_p,
+                              C.c_void_p], C.c_int),
     "nvfp4_mx_quantize": ([C.c_void_p, C.c_int32, C.c_int64, C.c_int64, C.c_void_p,
                            C.c_void_p, C.c_void_p], C.c_int),
     "nvfp4_gemm_mx": ([C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_int64,
@@ -247,6 +252,42 @@ def gemm_w4a4(a: NVFP4Tensor, w: NVFP4Tensor, out_dtype=torch.bfloat16,
     _check(lib().nvfp4_gemm_w4a4(C.byref(ca), C.byref(cw), _dev(out, "out"), _DT[out.dtype],
                                  None if amax_out is None else amax_out.data_ptr(),
                                  _stream(stream)))
+    return out
+
+
+def lora_down(x: torch.Tensor, a: torch.Tensor, out: torch.Tensor | None = None,
+              stream=None) -> torch.Tensor:
+    """nvfp4_lora_down: XA = bf16(x A^T); x [M, K], a [r, K] bfloat16."""
+    if x.dtype != torch.bfloat16 or a.dtype != torch.bfloat16 or x.dim() != 2 or a.dim() != 2:
+        raise ValueError("lora_down expects 2-D bfloat16 x and a")
+    M, K = x.shape
+    r = a.shape[0]
+    if a.shape[1] != K:
+        raise ValueError("lora_down: K mismatch")
+    if out is None:
+        out = torch.empty((M, r), dtype=torch.bfloat16, device=x.device)
+    _check(lib().nvfp4_lora_down(_dev(x, "x"), _dev(a, "a"), M, K, r, _dev(out, "out"),
+                                 _stream(stream)))
+    return out
+
+
+def gemm_w4a4_lora(a: NVFP4Tensor, w: NVFP4Tensor, xa: torch.Tensor, b: torch.Tensor,
+                   lora_scale: float, out_dtype=torch.bfloat16, out: torch.Tensor | None = None,
+                   amax_out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """nvfp4_gemm_w4a4_lora: W4A4 product plus lora_scale * XA B^T
+    (xa [M, r], b [N, r] bfloat16)."""
+    if xa.dtype != torch.bfloat16 or b.dtype != torch.bfloat16:
+        raise ValueError("xa and b must be bfloat16")
+    r = xa.shape[1]
+    if xa.shape[0] != a.rows or b.shape != (w.rows, r):
+        raise ValueError("gemm_w4a4_lora: adapter shapes do not match")
+    if out is None:
+        out = torch.empty((a.rows, w.rows), dtype=out_dtype, device=a.codes.device)
+    ca, cw = a.c(), w.c()
+    _check(lib().nvfp4_gemm_w4a4_lora(C.byref(ca), C.byref(cw), _dev(xa, "xa"), _dev(b, "b"), r,
+                                      float(lora_scale), _dev(out, "out"), _DT[out.dtype],
+                                      None if amax_out is None else amax_out.data_ptr(),
+                                      _stream(stream)))
     return out
 
 

@@ -255,8 +255,8 @@ int nvfp4_dequantize(const nvfp4_tensor *in, void *y, int32_t y_dtype, void *str
     return hip_status(e, "dequantize launch");
 }
 
-int nvfp4_gemm_w4a4(const nvfp4_tensor *a, const nvfp4_tensor *w, void *y, int32_t y_dtype,
-                    float *amax_out, void *stream) {
+static int check_gemm(const nvfp4_tensor *a, const nvfp4_tensor *w, const void *y,
+                      int32_t y_dtype, const float *amax_out) {
     int st = check_tensor(a, "gemm A");
     if (st) return st;
     st = check_tensor(w, "gemm W");
@@ -273,10 +273,51 @@ int nvfp4_gemm_w4a4(const nvfp4_tensor *a, const nvfp4_tensor *w, void *y, int32
     if (a->rows * w->rows > 0 && !y) return fail(NVFP4_EINVAL, "gemm: NULL y");
     if (!aligned16(y)) return fail(NVFP4_EALIGN, "gemm: y not 16-byte aligned");
     if (((uintptr_t)amax_out & 3u)) return fail(NVFP4_EALIGN, "gemm: amax_out misaligned");
+    return NVFP4_OK;
+}
+
+static bool lora_rank_ok(int64_t r) { return r == 16 || r == 32 || r == 64 || r == 128; }
+
+int nvfp4_gemm_w4a4(const nvfp4_tensor *a, const nvfp4_tensor *w, void *y, int32_t y_dtype,
+                    float *amax_out, void *stream) {
+    int st = check_gemm(a, w, y, y_dtype, amax_out);
+    if (st) return st;
     hipError_t e = nvfp4::launch_gemm_w4a4(a->codes, a->scales, a->s_dec, w->codes, w->scales,
                                            w->s_dec, a->rows, w->rows, a->cols, w->layout, y,
-                                           y_dtype, amax_out, (hipStream_t)stream);
+                                           y_dtype, amax_out, nullptr, nullptr, 0, 0.0f,
+                                           (hipStream_t)stream);
     return hip_status(e, "gemm launch");
+}
+
+int nvfp4_gemm_w4a4_lora(const nvfp4_tensor *a, const nvfp4_tensor *w, const void *xa_bf16,
+                         const void *b_bf16, int64_t r, float lora_scale, void *y,
+                         int32_t y_dtype, float *amax_out, void *stream) {
+    int st = check_gemm(a, w, y, y_dtype, amax_out);
+    if (st) return st;
+    if (!lora_rank_ok(r)) return fail(NVFP4_EINVAL, "gemm_lora: r must be 16, 32, 64 or 128");
+    if (a->rows * w->rows > 0 && (!xa_bf16 || !b_bf16))
+        return fail(NVFP4_EINVAL, "gemm_lora: NULL xa or b");
+    if (!aligned16(xa_bf16) || !aligned16(b_bf16))
+        return fail(NVFP4_EALIGN, "gemm_lora: xa and b must be 16-byte aligned");
+    hipError_t e = nvfp4::launch_gemm_w4a4(
+        a->codes, a->scales, a->s_dec, w->codes, w->scales, w->s_dec, a->rows, w->rows, a->cols,
+        w->layout, y, y_dtype, amax_out, (const uint16_t *)xa_bf16, (const uint16_t *)b_bf16, r,
+        lora_scale, (hipStream_t)stream);
+    return hip_status(e, "gemm_lora launch");
+}
+
+int nvfp4_lora_down(const void *x_bf16, const void *a_bf16, int64_t M, int64_t K, int64_t r,
+                    void *xa_bf16, void *stream) {
+    if (M < 0 || K <= 0) return fail(NVFP4_ESHAPE, "lora_down: bad shape");
+    if (K % 32) return fail(NVFP4_ESHAPE, "lora_down: K %% 32 != 0 (got %lld)", (long long)K);
+    if (!lora_rank_ok(r)) return fail(NVFP4_EINVAL, "lora_down: r must be 16, 32, 64 or 128");
+    if (M == 0) return ok();
+    if (!x_bf16 || !a_bf16 || !xa_bf16) return fail(NVFP4_EINVAL, "lora_down: NULL pointer");
+    if (!aligned16(x_bf16) || !aligned16(a_bf16) || !aligned16(xa_bf16))
+        return fail(NVFP4_EALIGN, "lora_down: pointers must be 16-byte aligned");
+    hipError_t e = nvfp4::launch_lora_down((const uint16_t *)x_bf16, (const uint16_t *)a_bf16, M,
+                                           K, r, (uint16_t *)xa_bf16, (hipStream_t)stream);
+    return hip_status(e, "lora_down launch");
 }
 
 // ---- MXFP4 speed reference ------------------------------------------------------

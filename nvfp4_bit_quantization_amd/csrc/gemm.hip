@@ -68,6 +68,7 @@ static_assert(kStage % 256 == 0, "stage alignment");
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void *lvoid;  // LDS
 
 struct GemmArgs {
@@ -288,11 +289,20 @@ __device__ __forceinline__ void step_all(f32x16 (&acc)[FM][FN], const Frag (&A)[
     (substep<S>(acc, A, B), ...);
 }
 
-template <bool OUT_BF16, bool KFAST, bool W2D>
+// LoRA epilogue operands (LORA = true): XA [M, r] and B [N, r] bf16, the
+// branch (lora_scale) * XA B^T added to every output.
+struct LoraArgs {
+    const uint16_t *xa;
+    const uint16_t *b;
+    int64_t r;
+    float scale;
+};
+
+template <bool OUT_BF16, bool KFAST, bool W2D, bool LORA>
 __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float *__restrict__ a_sdec,
                                                         const float *__restrict__ w_sdec,
                                                         void *__restrict__ yv,
-                                                        float *__restrict__ amax_out) {
+                                                        float *__restrict__ amax_out, LoraArgs la) {
     const int64_t M = g.M, N = g.N, K = g.K;
     const int64_t tn_count = (N + BN - 1) / BN;
     const int64_t ntiles = ((M + BM - 1) / BM) * tn_count;
@@ -377,10 +387,26 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
         for (int j = 0; j < FN; ++j) {
             const int64_t col = nw + j * 32 + r;
             const int64_t rbase = mw + i * 32 + h * 4;
+            f32x16 lo;
+            if (LORA) {
+                // (XA rows of block i) x (B rows of block j)^T on the bf16 MFMA,
+                // 16 of r per step; rows past the edge are clamped, never stored
+                const int64_t xr = mw + i * 32 + r < M ? mw + i * 32 + r : M - 1;
+                const int64_t br = col < N ? col : N - 1;
+                const uint16_t *xp = la.xa + xr * la.r + h * 8;
+                const uint16_t *bp = la.b + br * la.r + h * 8;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) lo[e] = 0.0f;
+                for (int64_t q = 0; q < la.r; q += 16)
+                    lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(xp + q),
+                                                                 *(const bf16x8 *)(bp + q), lo, 0,
+                                                                 0, 0);
+            }
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int64_t row = rbase + (e >> 2) * 8 + (e & 3);
-                const float v = scale * acc[i][j][e];
+                float v = scale * acc[i][j][e];
+                if (LORA) v = __builtin_fmaf(la.scale, lo[e], v);
                 if (row < M && col < N) {
                     if (OUT_BF16) {
                         const __bf16 b = (__bf16)v;
@@ -402,20 +428,28 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
 hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_sdec,
                             const uint8_t *w_codes, const uint8_t *w_scales,
                             const float *w_sdec, int64_t M, int64_t N, int64_t K, int w_layout,
-                            void *y, int ydtype, float *amax_out, hipStream_t s) {
+                            void *y, int ydtype, float *amax_out, const uint16_t *lora_xa,
+                            const uint16_t *lora_b, int64_t lora_r, float lora_scale,
+                            hipStream_t s) {
     if (M == 0 || N == 0) return hipSuccess;
     const int64_t ntiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const dim3 grid((unsigned)ntiles);
     const GemmArgs g{a_codes, a_scales, w_codes, w_scales, M, N, K};
+    const LoraArgs la{lora_xa, lora_b, lora_r, lora_scale};
+    const bool lora = lora_xa != nullptr;
     // LDS path: K a multiple of the step, and buffer offsets that fit 31 bits
     const bool fast = K % BK == 0 && M * (K / 2) < ((int64_t)1 << 31) &&
                       N * (K / 2) < ((int64_t)1 << 31);
     static bool attr_set = false;
     if (!attr_set) {
-        const void *fns[4] = {(const void *)gemm_w4a4_kernel<true, true, true>,
-                              (const void *)gemm_w4a4_kernel<false, true, true>,
-                              (const void *)gemm_w4a4_kernel<true, true, false>,
-                              (const void *)gemm_w4a4_kernel<false, true, false>};
+        const void *fns[8] = {(const void *)gemm_w4a4_kernel<true, true, true, false>,
+                              (const void *)gemm_w4a4_kernel<false, true, true, false>,
+                              (const void *)gemm_w4a4_kernel<true, true, false, false>,
+                              (const void *)gemm_w4a4_kernel<false, true, false, false>,
+                              (const void *)gemm_w4a4_kernel<true, true, true, true>,
+                              (const void *)gemm_w4a4_kernel<false, true, true, true>,
+                              (const void *)gemm_w4a4_kernel<true, true, false, true>,
+                              (const void *)gemm_w4a4_kernel<false, true, false, true>};
         for (const void *f : fns) {
             hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
                                                kLdsBytes);
@@ -423,29 +457,115 @@ hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, con
         }
         attr_set = true;
     }
-#define NVFP4_GEMM(BF, KF, W2)                                                                \
-    NVFP4_LAUNCH("gemm_w4a4", (gemm_w4a4_kernel<BF, KF, W2>), grid, dim3(256),               \
-                 KF ? kLdsBytes : 0, s, g, a_sdec, w_sdec, y, amax_out)
-#define NVFP4_GEMM_K(BF, W2)        \
-    if (fast)                       \
-        NVFP4_GEMM(BF, true, W2);   \
-    else                            \
-        NVFP4_GEMM(BF, false, W2);
+#define NVFP4_GEMM(BF, KF, W2, LO)                                                            \
+    NVFP4_LAUNCH(LO ? "gemm_w4a4_lora" : "gemm_w4a4", (gemm_w4a4_kernel<BF, KF, W2, LO>), grid, \
+                 dim3(256), KF ? kLdsBytes : 0, s, g, a_sdec, w_sdec, y, amax_out, la)
+#define NVFP4_GEMM_K(BF, W2, LO)     \
+    if (fast)                        \
+        NVFP4_GEMM(BF, true, W2, LO); \
+    else                             \
+        NVFP4_GEMM(BF, false, W2, LO);
+#define NVFP4_GEMM_W(BF, LO)             \
+    if (w_layout) {                      \
+        NVFP4_GEMM_K(BF, true, LO)       \
+    } else {                             \
+        NVFP4_GEMM_K(BF, false, LO)      \
+    }
     if (ydtype == kBF16) {
-        if (w_layout) {
-            NVFP4_GEMM_K(true, true)
+        if (lora) {
+            NVFP4_GEMM_W(true, true)
         } else {
-            NVFP4_GEMM_K(true, false)
+            NVFP4_GEMM_W(true, false)
         }
     } else {
-        if (w_layout) {
-            NVFP4_GEMM_K(false, true)
+        if (lora) {
+            NVFP4_GEMM_W(false, true)
         } else {
-            NVFP4_GEMM_K(false, false)
+            NVFP4_GEMM_W(false, false)
         }
     }
+#undef NVFP4_GEMM_W
 #undef NVFP4_GEMM_K
 #undef NVFP4_GEMM
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// LoRA down projection XA = bf16(X A^T)
+// ---------------------------------------------------------------------------
+
+// Workgroup = 16 rows of X; its 4 waves split K into quarters (32-deep
+// steps) and each accumulates 16 x r on the 16x16x32 bf16 MFMA; the quarters
+// are added in LDS in wave order and stored as bf16 (nearest-even).  Lane
+// (c = l & 15, g = l >> 4) holds row c of the X fragment and of each A
+// fragment, K values 8g .. 8g + 7 of the step; the output lane holds column
+// c, rows 4g .. 4g + 3.  Rows past M are clamped, never stored.
+template <int NB>  // r = 16 * NB
+__global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t *__restrict__ X,
+                                                        const uint16_t *__restrict__ A, int64_t M,
+                                                        int64_t K, uint16_t *__restrict__ XA) {
+    constexpr int r = 16 * NB;
+    __shared__ f32x4 part[4][NB][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = lane & 15, g = lane >> 4;
+    const int64_t m0 = (int64_t)blockIdx.x * 16;
+    const int64_t xr = m0 + c < M ? m0 + c : M - 1;
+    const int64_t steps = K / 32;
+    const int64_t s0 = steps * wave / 4, s1 = steps * (wave + 1) / 4;
+    f32x4 acc[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const uint16_t *xp = X + xr * K + g * 8;
+    const uint16_t *ap = A + (int64_t)c * K + g * 8;
+    // four steps of loads in flight before their MFMAs (steps past s1 are
+    // clamped to s1 - 1 and their products skipped)
+    for (int64_t st = s0; st < s1; st += 4) {
+        bf16x8 xf[4], af[4][NB];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t su = st + u < s1 ? st + u : s1 - 1;
+            xf[u] = *(const bf16x8 *)(xp + su * 32);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) af[u][j] = *(const bf16x8 *)(ap + (int64_t)j * 16 * K + su * 32);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (st + u >= s1) break;
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[u], af[u][j], acc[j], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) part[wave][j][lane] = acc[j];
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        const f32x4 v = ((part[0][j][lane] + part[1][j][lane]) + part[2][j][lane]) + part[3][j][lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t row = m0 + g * 4 + e;
+            if (row < M) ((__bf16 *)XA)[row * r + j * 16 + c] = (__bf16)v[e];
+        }
+    }
+}
+
+hipError_t launch_lora_down(const uint16_t *x, const uint16_t *a, int64_t M, int64_t K, int64_t r,
+                            uint16_t *xa, hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    const dim3 grid((unsigned)((M + 15) / 16));
+#define NVFP4_LD(NB) \
+    NVFP4_LAUNCH("lora_down", lora_down_kernel<NB>, grid, dim3(256), 0, s, x, a, M, K, xa)
+    switch (r) {
+    case 16: NVFP4_LD(1); break;
+    case 32: NVFP4_LD(2); break;
+    case 64: NVFP4_LD(4); break;
+    case 128: NVFP4_LD(8); break;
+    default: return hipErrorInvalidValue;
+    }
+#undef NVFP4_LD
     return hipGetLastError();
 }
 
