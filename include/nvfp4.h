@@ -293,8 +293,9 @@ int nvfp4_kv_begin_shot(nvfp4_kv_ring *ring, int64_t chunk_idx);
  * slot (DeepRead summary: chunk-level KV quantization, keys K-smoothed).
  *   K, V: device bf16 [T_c, H, d].
  *   mu[h, c] = (float)(sum / T_c), the per-channel key sum taken in double
- *   over 64-token tiles (each in token order, tiles in order); K_s =
- *   RN(K - mu).  K_s and V are each quantized 1-D along (h, c) with one FP32
+ *   in a fixed order: tiles of 16 tokens, each summed in token order, then
+ *   the tile sums (zero padded to a power-of-two count) added pairwise level
+ *   by level; K_s = RN(K - mu).  K_s and V are each quantized 1-D along (h, c) with one FP32
  *   tensor scale per chunk.  Chunk 0 also fills the global-sink region and
  *   the first chunk of a shot fills the shot-sink region (byte copies of the
  *   leading sink tokens, written by the same kernel).  Advances next_chunk.

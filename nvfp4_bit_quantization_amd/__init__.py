@@ -374,8 +374,7 @@ class KVRing:
         self.mem = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
         off = (-self.mem.data_ptr()) % 256
         self._base = self.mem.data_ptr() + off
-        self.ws = torch.empty(kv_store_workspace_bytes(cfg) + 256, dtype=torch.uint8,
-                              device=device)
+        self.ws = torch.empty(kv_store_workspace_bytes(cfg), dtype=torch.uint8, device=device)
         self.ring = CKvRing()
         _check(lib().nvfp4_kv_ring_init(C.byref(self.ring), C.byref(c), C.c_void_p(self._base),
                                         nbytes))

@@ -66,7 +66,7 @@ constexpr int kStage = kBSOff + BN * 16;  // 64512 bytes
 constexpr int kLdsBytes = 2 * kStage;
 static_assert(kStage % 256 == 0, "stage alignment");
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void *lvoid;  // LDS

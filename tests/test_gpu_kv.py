@@ -75,6 +75,73 @@ def run_ring(nv, orc, cfg, cuts, steps, seed, full_check=True, sample_tokens=Non
     return ring, chunks
 
 
+def region(mem, off, T, HD):
+    """Arrays of one ring region at byte offset `off`: K codes, K scales, V
+    codes, V scales (each 256-byte aligned), mu, s_dec."""
+    a = lambda n: (n + 255) // 256 * 256
+    o = off
+    out = {}
+    for name, n in (("kc", T * HD // 2), ("ks", T * HD // 16), ("vc", T * HD // 2),
+                    ("vs", T * HD // 16)):
+        out[name] = mem[o:o + n]
+        o += a(n)
+    out["mu"] = mem[o:o + HD * 4].view(np.float32)
+    o += a(HD * 4)
+    out["sd"] = mem[o:o + 8].view(np.float32)
+    return out
+
+
+def ring_bytes(ring):
+    torch.cuda.synchronize()
+    return ring.mem.cpu().numpy()[ring._base - ring.mem.data_ptr():]
+
+
+def assert_region(reg, ref, ntok, HD):
+    """Region holding the first ntok tokens of the oracle's chunk `ref`."""
+    assert np.array_equal(reg["mu"], ref["mu"])
+    assert reg["sd"][0] == ref["sdk"] and reg["sd"][1] == ref["sdv"]
+    for name, per in (("kc", HD // 2), ("ks", HD // 16), ("vc", HD // 2), ("vs", HD // 16)):
+        got, want = reg[name], ref[name].ravel()[:ntok * per]
+        bad = np.flatnonzero(got[:ntok * per] != want)
+        assert bad.size == 0, f"{name}: {bad.size} bytes differ, first at {bad[:4]}"
+
+
+# (tokens per frame, frames per chunk, heads, head_dim, S_g, S_s): ragged last
+# 64-token node, chunks shorter than a tile, channel counts that are not
+# multiples of 128, a 1024-node key-mean tree (65536 tokens), sinks
+STORE_CASES = [
+    (40, 5, 3, 32, 2, 1),
+    (7, 1, 1, 16, 1, 0),
+    (16, 4, 2, 64, 1, 2),
+    (13, 10, 1, 48, 3, 2),
+    (125, 8, 5, 16, 3, 3),
+    (520, 8, 2, 128, 3, 3),
+    (880, 8, 3, 128, 3, 3),
+    (8192, 8, 1, 16, 1, 1),
+]
+
+
+@pytest.mark.parametrize("case", STORE_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_store_bit_exact_ragged_and_sinks(nv, orc, case):
+    """Slot and both sink copies after storing chunk 0 equal the oracle's
+    encoding byte for byte."""
+    Lf, Fc, H, d, Sg, Ss = case
+    T, HD = Lf * Fc, H * d
+    print("case: store", case, flush=True)
+    cfg = nv.KVConfig(tokens_per_frame=Lf, frames_per_chunk=Fc, heads=H, head_dim=d,
+                      sink_frames_global=Sg, sink_frames_shot=Ss, window_chunks=2)
+    ring = nv.KVRing(cfg)
+    Kg, Vg, K, V = chunk_inputs(2100 + T, 0, T, H, d)
+    ring.store_chunk(0, Kg, Vg)
+    ref = orc.kv_encode_chunk(K, V)
+    mem = ring_bytes(ring)
+    assert_region(region(mem, 0, T, HD), ref, T, HD)
+    if Sg:
+        assert_region(region(mem, ring.ring.gsink_offset, Sg * Lf, HD), ref, Sg * Lf, HD)
+    if Ss:
+        assert_region(region(mem, ring.ring.ssink_offset, Ss * Lf, HD), ref, Ss * Lf, HD)
+
+
 def test_store_chunk_ring_bytes_bit_exact(nv, orc):
     """Ring slot contents after one store equal the oracle's chunk encoding."""
     cfg = nv.KVConfig(tokens_per_frame=40, frames_per_chunk=5, heads=3, head_dim=32,
