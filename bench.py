@@ -454,6 +454,63 @@ def run_ring64s(nv, args, dev):
             "alg_bytes": alg}
 
 
+def run_cfg1(nv, dev, reps=50):
+    """The small configuration (launch-latency bound, reported in us): 1-D 4/6
+    quantize of fp32 4096x128 (amax + encode), dequantize back to fp32, and
+    the W4A4 GEMM 256x256x512."""
+    import torch
+
+    import synth
+
+    x = torch.from_numpy(synth.activations(1001, 0, 4096, 128, 0.01, 20.0)).to(dev)
+    q = nv.NVFP4Tensor.empty(4096, 128)
+    ws = torch.empty(nv.quantize_workspace_bytes(4096, 128), dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    A = torch.from_numpy(synth.activations(1001, 1, 256, 512, 0.01, 20.0)).to(dev)
+    W = torch.from_numpy(synth.weights(1001, 2, 256, 512)).to(dev)
+    qa, qw = nv.quantize(A), nv.quantize(W, layout=nv.LAYOUT_2D)
+    Y = torch.empty((256, 256), dtype=torch.float32, device=dev)
+    qms, _ = time_steps(lambda i: nv.quantize(x, out=q, workspace=ws), reps, 10)
+    dms, _ = time_steps(lambda i: nv.dequantize(q, out=y), reps, 10)
+    gms, _ = time_steps(lambda i: nv.gemm_w4a4(qa, qw, out=Y), reps, 10)
+    return {"quantize_us": round(qms * 1e3, 2), "dequantize_us": round(dms * 1e3, 2),
+            "gemm_256x256x512_us": round(gms * 1e3, 2),
+            "note": "launch-latency bound; a parity configuration, not a roofline one"}
+
+
+def sustained_sclk_mhz(nv, dev, seconds=0.6):
+    """Shader clock (MHz) reported by rocm-smi while W4A4 GEMMs run back to
+    back; None if rocm-smi is unavailable."""
+    import re
+    import subprocess
+    import threading
+
+    import torch
+
+    _, qa, qw, Y = setup_gemm(nv, dev)
+    stop = threading.Event()
+
+    def loop():
+        while not stop.is_set():
+            for _ in range(10):
+                nv.gemm_w4a4(qa, qw, out=Y)
+            torch.cuda.synchronize()
+
+    t = threading.Thread(target=loop)
+    t.start()
+    try:
+        time.sleep(seconds)
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=30)
+        m = re.search(r'"sclk clock speed:": "\((\d+)Mhz\)"', r.stdout)
+        return int(m.group(1)) if m else None
+    except (OSError, subprocess.SubprocessError):
+        return None
+    finally:
+        stop.set()
+        t.join()
+
+
 # --------------------------------------------------------------------------
 
 def main():
@@ -540,8 +597,25 @@ def main():
         lo = run_lora(nv, argparse.Namespace(steps=20, warmup=5, sets=args.sets), dev)
         sec["lora_r32_7040x3072x3072"] = {k: (round(v, 4) if isinstance(v, float) else v)
                                           for k, v in lo.items()}
+        # the same KV step with one buffer set: the chunk's 86.5 MB stay in the
+        # 256 MB last-level cache between steps (labelled warm)
+        wstep, _ = setup_kv_chunk(nv, argparse.Namespace(sets=1), dev)
+        wms, _ = time_steps(wstep, args.steps, args.warmup)
+        sec["kv_chunk_warm_cache_1_buffer_set"] = {"GB/s": round(alg_step / wms / 1e6, 1),
+                                                   "ms_per_step": round(wms, 5)}
+        sec["cfg1_4096x128_fp32_and_gemm_256x256x512"] = run_cfg1(nv, dev)
+        f = run_ffn(nv, argparse.Namespace(steps=5, warmup=2, sets=1), dev)
+        sec["ffn_7040x3072x14336_up_requantize_down"] = {
+            "TFLOP/s": round(f["tflops"], 1), "ms": round(f["ms"], 4),
+            "frac_mfma_peak": round(f["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
+            "kernels_us": {k: round(v[1] * 1e3, 2) for k, v in f["kernels"].items()}}
+        r = run_ring64s(nv, argparse.Namespace(steps=10, warmup=1, sets=args.sets), dev)
+        sec["ring64s_40_chunks_gather_and_store"] = {
+            "GB/s": round(r["gbs"], 1), "ms_per_40_chunks": round(r["ms"], 3),
+            "tokens_gathered": r["tokens_gathered"], "alg_bytes": r["alg_bytes"]}
         out["secondary"] = sec
         out["context_copy_GB/s"] = round(copy_gbs(dev), 1)
+        out["sclk_MHz_during_gemm"] = sustained_sclk_mhz(nv, dev)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_kv()

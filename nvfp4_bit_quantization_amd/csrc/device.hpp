@@ -113,7 +113,8 @@ __device__ __forceinline__ float div6_rn(float a) {
     const float q0 = a * c;
     const float r = __builtin_fmaf(-q0, 6.0f, a);
     float q = __builtin_fmaf(r, c, q0);
-    if (a < 0x1p-125f) q = a / 6.0f;
+    // the division is skipped by the whole wave unless one of its lanes needs it
+    if (__builtin_amdgcn_ballot_w64(a < 0x1p-125f)) q = (a < 0x1p-125f) ? a / 6.0f : q;
     return q;
 }
 

@@ -319,16 +319,48 @@ __global__ __launch_bounds__(64) void kv_finalize_kernel(KvWs w, int64_t nt64, i
     if (lane == 0) w.kpart[blockIdx.x] = amax;
 }
 
+// Raw 16-element bf16 block at byte offset `off` of a buffer (zero past its end).
+__device__ __forceinline__ Raw16Bf16 block_load(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    Raw16Bf16 r;
+    r.a = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    r.b = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0);
+    return r;
+}
+
+// Destination of one tensor's blocks: codes (8 bytes per block) and scales
+// (1 byte per block) of the slot and of the two sink copies, as buffer
+// descriptors whose sizes are the blocks each holds, so a store past them is
+// dropped by the hardware range check.
+struct EncDst {
+    __amdgpu_buffer_rsrc_t c, s, gc, gs, sc, ss;
+};
+
+__device__ __forceinline__ void block_store(const EncDst &d, bool sinks, uint32_t b, uint32_t lo,
+                                            uint32_t hi, uint32_t sc) {
+    const u32x2 q = u32x2{lo, hi};
+    __builtin_amdgcn_raw_buffer_store_b64(q, d.c, b * 8, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, d.s, b, 0, 0);
+    if (sinks) {  // uniform: the chunk writes a sink copy
+        __builtin_amdgcn_raw_buffer_store_b64(q, d.gc, b * 8, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, d.gs, b, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(q, d.sc, b * 8, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, d.ss, b, 0, 0);
+    }
+}
+
 // One lane per 1x16 block along the (head, dim) axis; blockIdx.y = 0: keys
 // (K_s = RN(K - mu)), 1: values.  The first two blocks of each lane are
 // loaded before the prologue, which reduces the key / value amax partials,
 // derives both tensor scales (workgroup (0,0) stores the decode scales into
 // the slot and the sink copies) and builds the (S, r) table of the
-// workgroup's tensor; afterwards each lane keeps two blocks in flight.  When
-// the grid stride is a multiple of the blocks per token (MU_FIXED) every
-// block of a lane starts at the same channel, and the lane holds its 16 key
-// means in registers; otherwise they are re-read per block.  Blocks below
-// the sink length are also written to the sink copies.
+// workgroup's tensor; afterwards each lane keeps two blocks in flight, with
+// the loop unrolled three times so the three block registers rotate without
+// copies.  Loads and stores are raw buffer accesses with 32-bit offsets:
+// a block past the end loads as zero and its stores are dropped by the
+// range check (also how only the blocks below the sink length reach the
+// sink copies).  When the grid stride is a multiple of the blocks per token
+// (MU_FIXED) every block of a lane starts at the same channel, and the lane
+// holds its 16 key means in registers; otherwise they are re-read per block.
 template <bool FOUR_OVER_SIX, bool MU_FIXED>
 __global__ __launch_bounds__(256) void kv_encode_kernel(
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, int64_t nblk, int64_t HD,
@@ -338,17 +370,20 @@ __global__ __launch_bounds__(256) void kv_encode_kernel(
     __shared__ float red[2][4];
     __shared__ float sh[4];
     const int which = blockIdx.y;  // 0: keys, 1: values
-    const uint16_t *x = which ? V : K;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    Raw16Bf16 r0, r1;
-    if (b < nblk) load_raw16(x + b * 16, r0);
-    if (b + stride < nblk) load_raw16(x + (b + stride) * 16, r1);
+    // nblk * 32 = T * HD * 2 < 2^32 bytes; block offsets are clamped to the
+    // end so that they never wrap
+    const uint32_t nb = (uint32_t)nblk;
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(which ? V : K), (short)0, (int)(nb * 32u), kBufferWord3);
+    const uint32_t stride = gridDim.x * blockDim.x;
+    uint32_t b = blockIdx.x * blockDim.x + threadIdx.x;
+    auto off = [nb](uint32_t blk) { return (blk < nb ? blk : nb) * 32u; };
+    Raw16Bf16 ra = block_load(xr, off(b)), rb = block_load(xr, off(b + stride)), rc;
     // channel of the block's first element, advanced without division: (16 b) mod HD
-    int64_t ch0 = (b * 16) % HD;
-    const int64_t step = (stride * 16) % HD;
+    int64_t ch0 = ((int64_t)b * 16) % HD;
+    const int64_t step = ((int64_t)stride * 16) % HD;
     float mu[16];
-    if (MU_FIXED && which == 0 && b < nblk) {
+    if (MU_FIXED && which == 0 && b < nb) {
         Raw16F32 m;
         load_raw16(slot.mu + ch0, m);
         unpack16(m, mu);
@@ -391,17 +426,22 @@ __global__ __launch_bounds__(256) void kv_encode_kernel(
     const float s_dec = sh[2 * which + 1];
     for (int c = threadIdx.x; c < 128; c += blockDim.x) lut[c] = scale_entry((uint32_t)c, s_dec);
     __syncthreads();
-    uint2 *codes = (uint2 *)(which ? slot.vc : slot.kc);
-    uint8_t *scales = which ? slot.vs : slot.ks;
-    uint2 *gcodes = (uint2 *)(which ? gsink.vc : gsink.kc);
-    uint8_t *gscales = which ? gsink.vs : gsink.ks;
-    uint2 *scodes = (uint2 *)(which ? ssink.vc : ssink.kc);
-    uint8_t *sscales = which ? ssink.vs : ssink.ks;
-    for (; b < nblk; b += stride) {
-        // two blocks ahead are in flight while this one is encoded
-        const Raw16Bf16 r = r0;
-        r0 = r1;
-        if (b + 2 * stride < nblk) load_raw16(x + (b + 2 * stride) * 16, r1);
+    EncDst d;
+    const uint32_t gb = (uint32_t)g_blk, sb = (uint32_t)s_blk;
+    d.c = __builtin_amdgcn_make_buffer_rsrc((void *)(which ? slot.vc : slot.kc), (short)0,
+                                            (int)(nb * 8u), kBufferWord3);
+    d.s = __builtin_amdgcn_make_buffer_rsrc((void *)(which ? slot.vs : slot.ks), (short)0, (int)nb,
+                                            kBufferWord3);
+    d.gc = __builtin_amdgcn_make_buffer_rsrc((void *)(which ? gsink.vc : gsink.kc), (short)0,
+                                             (int)(gb * 8u), kBufferWord3);
+    d.gs = __builtin_amdgcn_make_buffer_rsrc((void *)(which ? gsink.vs : gsink.ks), (short)0,
+                                             (int)gb, kBufferWord3);
+    d.sc = __builtin_amdgcn_make_buffer_rsrc((void *)(which ? ssink.vc : ssink.kc), (short)0,
+                                             (int)(sb * 8u), kBufferWord3);
+    d.ss = __builtin_amdgcn_make_buffer_rsrc((void *)(which ? ssink.vs : ssink.ks), (short)0,
+                                             (int)sb, kBufferWord3);
+    const bool sinks = gb > 0 || sb > 0;
+    auto encode = [&](const Raw16Bf16 &r, uint32_t blk) {
         float v[16];
         unpack16(r, v);
         if (which == 0) {
@@ -417,16 +457,17 @@ __global__ __launch_bounds__(256) void kv_encode_kernel(
         }
         uint32_t lo, hi, sc;
         encode_block16<FOUR_OVER_SIX>(v, s_enc, lut, lo, hi, sc);
-        codes[b] = make_uint2(lo, hi);
-        scales[b] = (uint8_t)sc;
-        if (b < g_blk) {
-            gcodes[b] = make_uint2(lo, hi);
-            gscales[b] = (uint8_t)sc;
-        }
-        if (b < s_blk) {
-            scodes[b] = make_uint2(lo, hi);
-            sscales[b] = (uint8_t)sc;
-        }
+        block_store(d, sinks, blk, lo, hi, sc);
+    };
+    // blocks b, b + stride, b + 2 stride per iteration (past nblk: zero
+    // loads, dropped stores)
+    for (; b < nb; b += 3 * stride) {
+        rc = block_load(xr, off(b + 2 * stride));
+        encode(ra, b);
+        ra = block_load(xr, off(b + 3 * stride));
+        encode(rb, b + stride);
+        rb = block_load(xr, off(b + 4 * stride));
+        encode(rc, b + 2 * stride);
     }
 }
 
