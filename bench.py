@@ -478,6 +478,46 @@ def run_cfg1(nv, dev, reps=50):
             "note": "launch-latency bound; a parity configuration, not a roofline one"}
 
 
+def attention_context(nv, dev, reps=3):
+    """Context for fusing the dequantization into attention: one steady-state
+    step of the 64 s ring (7040 queries against the 33,440-token effective
+    set, 24 heads of 128) timed as the gather alone and as torch's flash
+    attention on the gathered bf16 K/V.  Only the flash kernel is allowed (no
+    fallback to the math path); None if it is unavailable."""
+    import torch
+
+    import synth
+
+    cfg = nv.KVConfig()
+    ring = nv.KVRing(cfg)
+    kb, vb = synth.kv_chunk(1006, 0, KV_T, KV_H, KV_D)
+    K, V = bf16_from_bits(kb, dev), bf16_from_bits(vb, dev)
+    for t in range(15):  # steps 15..19 gather 33,440 tokens
+        if t % 10 == 0:
+            ring.begin_shot(t)
+        ring.store_chunk(t, K, V)
+    n = ring.effective_tokens(15)
+    Ko = torch.empty((n, KV_H, KV_D), dtype=torch.bfloat16, device=dev)
+    Vo = torch.empty_like(Ko)
+    gms, _ = time_steps(lambda i: ring.gather_window(15, Ko, Vo), 10, 3)
+    try:
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+
+        q = torch.randn((1, KV_H, KV_T, KV_D), dtype=torch.bfloat16, device=dev)
+        k = Ko.permute(1, 0, 2).contiguous().unsqueeze(0)
+        v = Vo.permute(1, 0, 2).contiguous().unsqueeze(0)
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            ams, _ = time_steps(
+                lambda i: torch.nn.functional.scaled_dot_product_attention(q, k, v), reps, 1)
+    except (RuntimeError, ImportError) as e:
+        return {"gather_us": round(gms * 1e3, 2), "tokens": n, "flash_attention": None,
+                "note": f"flash attention unavailable: {type(e).__name__}"}
+    flops = 4.0 * KV_T * n * KV_D * KV_H
+    return {"tokens": n, "gather_us": round(gms * 1e3, 2), "flash_attention_ms": round(ams, 3),
+            "flash_attention_TFLOP/s": round(flops / ams / 1e9, 1),
+            "gather_share_of_gather_plus_attention": round(gms / (gms + ams), 4)}
+
+
 def sustained_sclk_mhz(nv, dev, seconds=0.6):
     """Shader clock (MHz) reported by rocm-smi while W4A4 GEMMs run back to
     back; None if rocm-smi is unavailable."""
@@ -613,6 +653,7 @@ def main():
         sec["ring64s_40_chunks_gather_and_store"] = {
             "GB/s": round(r["gbs"], 1), "ms_per_40_chunks": round(r["ms"], 3),
             "tokens_gathered": r["tokens_gathered"], "alg_bytes": r["alg_bytes"]}
+        sec["attention_context_ring_step_33440_tokens"] = attention_context(nv, dev)
         out["secondary"] = sec
         out["context_copy_GB/s"] = round(copy_gbs(dev), 1)
         out["sclk_MHz_during_gemm"] = sustained_sclk_mhz(nv, dev)
