@@ -254,6 +254,21 @@ __device__ __forceinline__ void unpack16(const Raw16F32 &r, float (&x)[16]) {
         x[4 * i + 3] = v[i].w;
     }
 }
+// The same blocks by raw buffer loads at byte offset `off` (a block past the
+// descriptor's end reads as zero).
+__device__ __forceinline__ void buffer_load16(__amdgpu_buffer_rsrc_t rs, uint32_t off,
+                                              Raw16Bf16 &r) {
+    r.a = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    r.b = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0);
+}
+__device__ __forceinline__ void buffer_load16(__amdgpu_buffer_rsrc_t rs, uint32_t off,
+                                              Raw16F32 &r) {
+    r.a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    r.b = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0));
+    r.c = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 32, 0, 0));
+    r.d = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 48, 0, 0));
+}
+
 template <typename T> struct Raw16Of;
 template <> struct Raw16Of<uint16_t> { typedef Raw16Bf16 type; };
 template <> struct Raw16Of<float> { typedef Raw16F32 type; };

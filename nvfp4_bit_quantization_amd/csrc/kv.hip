@@ -322,8 +322,7 @@ __global__ __launch_bounds__(64) void kv_finalize_kernel(KvWs w, int64_t nt64, i
 // Raw 16-element bf16 block at byte offset `off` of a buffer (zero past its end).
 __device__ __forceinline__ Raw16Bf16 block_load(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
     Raw16Bf16 r;
-    r.a = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-    r.b = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0);
+    buffer_load16(rs, off, r);
     return r;
 }
 

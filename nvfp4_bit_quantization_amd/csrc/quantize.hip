@@ -10,11 +10,9 @@
 // Work split (HBM-bound streaming; one pass for the tensor amax, one for the
 // encode):
 //   amax_kernel      16-byte loads, grid-stride, one partial max per workgroup
-//   encode1d_kernel  each lane owns 8 consecutive elements (half a 1x16 block),
-//                    a lane pair owns a block; the block amax and the two
-//                    half-block errors meet through one DPP swap; both
-//                    candidates are evaluated in registers; packed nibble
-//                    dword stores (coalesced), one scale byte per pair
+//   encode1d_kernel  one lane per 1x16 block (encode_block16: both
+//                    candidates in registers), two blocks in flight, raw
+//                    buffer loads and stores
 //   encode2d_kernel  32 lanes own a 16x16 tile (lane pair = tile row)
 //   dequant_kernel   8 elements per lane, 16-byte stores
 #include "device.hpp"
@@ -140,50 +138,61 @@ __device__ __forceinline__ void candidate(const float (&x)[8], float am, float s
     err_half = half_block_error(x, q, sr.x);
 }
 
-// Encode the half block held by this lane; the partner lane (lane ^ 1) holds
-// the other half of the same 1x16 block.  Returns the code dword and the
-// chosen scale byte (identical in both lanes).
-template <bool FOUR_OVER_SIX>
-__device__ __forceinline__ void encode_half_block(const float (&x)[8], float s_enc,
-                                                  const f32x2 *lut, uint32_t &codes,
-                                                  uint32_t &scale) {
-    float am = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(x[i]));
-    am = fmaxf(am, swap_pair(am));
-    uint32_t sc6, q6;
-    float e6;
-    candidate<6>(x, am, s_enc, lut, sc6, q6, e6);
-    if (!FOUR_OVER_SIX) {
-        codes = q6;
-        scale = sc6;
-        return;
-    }
-    uint32_t sc4, q4;
-    float e4;
-    candidate<4>(x, am, s_enc, lut, sc4, q4, e4);
-    // block error = RN(E_lo + E_hi); addition is commutative, so both lanes agree
-    e6 = e6 + swap_pair(e6);
-    e4 = e4 + swap_pair(e4);
-    const bool pick4 = e4 < e6;
-    codes = pick4 ? q4 : q6;
-    scale = pick4 ? sc4 : sc6;
-}
-
 // ---------------------------------------------------------------------------
 // 1-D encode: one lane per 1x16 block, two blocks in flight per lane
 // ---------------------------------------------------------------------------
 
-// With RHT every block is first transformed by rht16 (signs).
-template <typename T, bool FOUR_OVER_SIX, bool RHT>
+// With RHT every block is first transformed by rht16 (signs).  BUF (arrays
+// below 2^31 bytes): raw buffer loads and stores with 32-bit offsets, the
+// first two blocks of each lane requested before the prologue and two kept
+// in flight, the loop unrolled three times so the block registers rotate
+// without copies; a block past the end loads as zero and its stores are
+// dropped by the range check.  Otherwise: two blocks per iteration by
+// pointer.
+template <typename T, bool FOUR_OVER_SIX, bool RHT, bool BUF>
 __global__ __launch_bounds__(256) void encode1d_kernel(
     const T *__restrict__ x, int64_t nblk, const float *__restrict__ partials, int np,
     const float *__restrict__ amax_in, uint2 *__restrict__ codes, uint8_t *__restrict__ scales,
     float *__restrict__ s_dec_out, uint32_t signs) {
     __shared__ f32x2 lut[128];
+    typedef typename Raw16Of<T>::type Raw;
+    if (BUF) {
+        constexpr uint32_t BB = 16 * sizeof(T);  // bytes per block
+        const uint32_t nb = (uint32_t)nblk, stride = gridDim.x * blockDim.x;
+        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)x, (short)0, (int)(nb * BB), kBufferWord3);
+        auto off = [nb](uint32_t blk) { return (blk < nb ? blk : nb) * BB; };
+        uint32_t b = blockIdx.x * blockDim.x + threadIdx.x;
+        Raw ra, rb, rc;
+        buffer_load16(xr, off(b), ra);
+        buffer_load16(xr, off(b + stride), rb);
+        float s_enc;
+        encode_prologue(partials, np, amax_in, s_dec_out, lut, s_enc);
+        const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)codes, (short)0, (int)(nb * 8u), kBufferWord3);
+        const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)scales, (short)0, (int)nb, kBufferWord3);
+        auto encode = [&](const Raw &r, uint32_t blk) {
+            float v[16];
+            uint32_t lo, hi, sc;
+            unpack16(r, v);
+            if (RHT) rht16(v, signs);
+            encode_block16<FOUR_OVER_SIX>(v, s_enc, lut, lo, hi, sc);
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, cr, blk * 8, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, sr, blk, 0, 0);
+        };
+        for (; b < nb; b += 3 * stride) {
+            buffer_load16(xr, off(b + 2 * stride), rc);
+            encode(ra, b);
+            buffer_load16(xr, off(b + 3 * stride), ra);
+            encode(rb, b + stride);
+            buffer_load16(xr, off(b + 4 * stride), rb);
+            encode(rc, b + 2 * stride);
+        }
+        return;
+    }
     float s_enc;
     encode_prologue(partials, np, amax_in, s_dec_out, lut, s_enc);
-    typedef typename Raw16Of<T>::type Raw;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += 2 * stride) {
         const int64_t b2 = b + stride;
@@ -329,13 +338,18 @@ hipError_t launch_encode(const void *x, int dtype, int64_t rows, int64_t cols, i
         const int64_t nblk = n / 16;
         const int g = grid_for(nblk, 256, kStreamGrid);
         uint2 *c64 = (uint2 *)codes;
-#define L1(T, F)                                                                          \
-    NVFP4_LAUNCH("encode1d", (encode1d_kernel<T, F, false>), dim3(g), dim3(256), 0, s,        \
-                 (const T *)x, nblk, partials, np, amax_in, c64, scales, s_dec, 0u)
+        const bool buf = n * (dtype == kF32 ? 4 : 2) < ((int64_t)1 << 31);
+#define L1(T, F)                                                                            \
+    if (buf)                                                                                \
+        NVFP4_LAUNCH("encode1d", (encode1d_kernel<T, F, false, true>), dim3(g), dim3(256), 0, \
+                     s, (const T *)x, nblk, partials, np, amax_in, c64, scales, s_dec, 0u);   \
+    else                                                                                    \
+        NVFP4_LAUNCH("encode1d", (encode1d_kernel<T, F, false, false>), dim3(g), dim3(256), 0,\
+                     s, (const T *)x, nblk, partials, np, amax_in, c64, scales, s_dec, 0u);
         if (dtype == kF32) {
-            if (f46) L1(float, true); else L1(float, false);
+            if (f46) { L1(float, true) } else { L1(float, false) }
         } else {
-            if (f46) L1(uint16_t, true); else L1(uint16_t, false);
+            if (f46) { L1(uint16_t, true) } else { L1(uint16_t, false) }
         }
 #undef L1
     } else {
@@ -374,13 +388,18 @@ hipError_t launch_quantize_rht(const void *x, int dtype, int64_t rows, int64_t c
     }
     const int g = grid_for(nblk, 256, kStreamGrid);
     uint2 *c64 = (uint2 *)codes;
-#define LR(T, F)                                                                            \
-    NVFP4_LAUNCH("encode1d_rht", (encode1d_kernel<T, F, true>), dim3(g), dim3(256), 0, s,   \
-                 (const T *)x, nblk, partials, np, amax_in, c64, scales, s_dec, signs)
+    const bool buf = rows * cols * (dtype == kF32 ? 4 : 2) < ((int64_t)1 << 31);
+#define LR(T, F)                                                                               \
+    if (buf)                                                                                   \
+        NVFP4_LAUNCH("encode1d_rht", (encode1d_kernel<T, F, true, true>), dim3(g), dim3(256), 0, \
+                     s, (const T *)x, nblk, partials, np, amax_in, c64, scales, s_dec, signs);   \
+    else                                                                                       \
+        NVFP4_LAUNCH("encode1d_rht", (encode1d_kernel<T, F, true, false>), dim3(g), dim3(256),   \
+                     0, s, (const T *)x, nblk, partials, np, amax_in, c64, scales, s_dec, signs);
     if (dtype == kF32) {
-        if (search == 1) LR(float, true); else LR(float, false);
+        if (search == 1) { LR(float, true) } else { LR(float, false) }
     } else {
-        if (search == 1) LR(uint16_t, true); else LR(uint16_t, false);
+        if (search == 1) { LR(uint16_t, true) } else { LR(uint16_t, false) }
     }
 #undef LR
     return hipGetLastError();
