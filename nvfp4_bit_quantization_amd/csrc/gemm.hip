@@ -381,44 +381,69 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
 
     const float scale = (*a_sdec) * (*w_sdec);
     float amax = 0.0f;  // max |stored y| of this lane
+    // LoRA: (XA rows of block i) x (B rows of block j)^T on the bf16 MFMA, 16
+    // of r per step, for two row blocks x three column blocks at a time; each
+    // step loads those 2 + 3 fragments at once (rows past the edge are
+    // clamped, never stored)
+    constexpr int FH = FM / 2;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int ih = 0; ih < 2; ++ih) {
+        f32x16 lo[FH][FN];
+        if (LORA) {
+            const uint16_t *xp[FH], *bp[FN];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int64_t col = nw + j * 32 + r;
-            const int64_t rbase = mw + i * 32 + h * 4;
-            f32x16 lo;
-            if (LORA) {
-                // (XA rows of block i) x (B rows of block j)^T on the bf16 MFMA,
-                // 16 of r per step; rows past the edge are clamped, never stored
-                const int64_t xr = mw + i * 32 + r < M ? mw + i * 32 + r : M - 1;
-                const int64_t br = col < N ? col : N - 1;
-                const uint16_t *xp = la.xa + xr * la.r + h * 8;
-                const uint16_t *bp = la.b + br * la.r + h * 8;
+            for (int i = 0; i < FH; ++i) {
+                const int64_t row = mw + (ih * FH + i) * 32 + r;
+                xp[i] = la.xa + (row < M ? row : M - 1) * la.r + h * 8;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) lo[e] = 0.0f;
-                for (int64_t q = 0; q < la.r; q += 16)
-                    lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(xp + q),
-                                                                 *(const bf16x8 *)(bp + q), lo, 0,
-                                                                 0, 0);
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) lo[i][j][e] = 0.0f;
             }
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int64_t row = rbase + (e >> 2) * 8 + (e & 3);
-                float v = scale * acc[i][j][e];
-                if (LORA) v = __builtin_fmaf(la.scale, lo[e], v);
-                if (row < M && col < N) {
-                    if (OUT_BF16) {
-                        const __bf16 b = (__bf16)v;
-                        ((__bf16 *)yv)[row * N + col] = b;
-                        amax = fmaxf(amax, fabsf((float)b));
-                    } else {
-                        ((float *)yv)[row * N + col] = v;
-                        amax = fmaxf(amax, fabsf(v));
+            for (int j = 0; j < FN; ++j) {
+                const int64_t col = nw + j * 32 + r;
+                bp[j] = la.b + (col < N ? col : N - 1) * la.r + h * 8;
+            }
+            for (int64_t q = 0; q < la.r; q += 16) {
+                bf16x8 xf[FH], bfr[FN];
+#pragma unroll
+                for (int i = 0; i < FH; ++i) xf[i] = *(const bf16x8 *)(xp[i] + q);
+#pragma unroll
+                for (int j = 0; j < FN; ++j) bfr[j] = *(const bf16x8 *)(bp[j] + q);
+#pragma unroll
+                for (int i = 0; i < FH; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        lo[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf[i], bfr[j],
+                                                                           lo[i][j], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int ii = 0; ii < FH; ++ii)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int i = ih * FH + ii;
+                const int64_t col = nw + j * 32 + r;
+                const int64_t rbase = mw + i * 32 + h * 4;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int64_t row = rbase + (e >> 2) * 8 + (e & 3);
+                    float v = scale * acc[i][j][e];
+                    if (LORA) v = __builtin_fmaf(la.scale, lo[ii][j][e], v);
+                    if (row < M && col < N) {
+                        if (OUT_BF16) {
+                            const __bf16 b = (__bf16)v;
+                            ((__bf16 *)yv)[row * N + col] = b;
+                            amax = fmaxf(amax, fabsf((float)b));
+                        } else {
+                            ((float *)yv)[row * N + col] = v;
+                            amax = fmaxf(amax, fabsf(v));
+                        }
                     }
                 }
             }
-        }
+    }
     if (amax_out) {
         amax = wave_max(amax);
         if (lane == 0) atomicMax((unsigned int *)amax_out, __float_as_uint(amax));
@@ -494,70 +519,99 @@ hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, con
 // LoRA down projection XA = bf16(X A^T)
 // ---------------------------------------------------------------------------
 
-// Workgroup = 16 rows of X; its 4 waves split K into quarters (32-deep
-// steps) and each accumulates 16 x r on the 16x16x32 bf16 MFMA; the quarters
-// are added in LDS in wave order and stored as bf16 (nearest-even).  Lane
-// (c = l & 15, g = l >> 4) holds row c of the X fragment and of each A
-// fragment, K values 8g .. 8g + 7 of the step; the output lane holds column
-// c, rows 4g .. 4g + 3.  Rows past M are clamped, never stored.
-template <int NB>  // r = 16 * NB
+// Workgroup = 16 ROWT rows of X; its 4 waves split K into quarters
+// (32-deep steps) and each accumulates (16 ROWT) x r on the 16x16x32 bf16
+// MFMA, so every A fragment a wave loads serves ROWT row tiles; the
+// quarters are added in LDS in wave order and stored as bf16
+// (nearest-even).  Lane (c = l & 15, g = l >> 4) holds row c of each X
+// fragment and of each A fragment, K values 8g .. 8g + 7 of the step; the
+// output lane holds column c, rows 4g .. 4g + 3 of a tile.  Rows past M are
+// clamped, never stored.
+template <int NB, int ROWT>  // r = 16 * NB
 __global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t *__restrict__ X,
                                                         const uint16_t *__restrict__ A, int64_t M,
                                                         int64_t K, uint16_t *__restrict__ XA) {
     constexpr int r = 16 * NB;
-    __shared__ f32x4 part[4][NB][64];
+    constexpr int U = NB * ROWT <= 8 ? 4 : 2;  // steps of loads in flight
+    __shared__ f32x4 part[4][ROWT][NB][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = lane & 15, g = lane >> 4;
-    const int64_t m0 = (int64_t)blockIdx.x * 16;
-    const int64_t xr = m0 + c < M ? m0 + c : M - 1;
+    const int64_t m0 = (int64_t)blockIdx.x * 16 * ROWT;
     const int64_t steps = K / 32;
     const int64_t s0 = steps * wave / 4, s1 = steps * (wave + 1) / 4;
-    f32x4 acc[NB];
+    f32x4 acc[ROWT][NB];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    const uint16_t *xp = X + xr * K + g * 8;
+    for (int t = 0; t < ROWT; ++t)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[t][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const uint16_t *xp[ROWT];
+#pragma unroll
+    for (int t = 0; t < ROWT; ++t) {
+        const int64_t xr = m0 + t * 16 + c < M ? m0 + t * 16 + c : M - 1;
+        xp[t] = X + xr * K + g * 8;
+    }
     const uint16_t *ap = A + (int64_t)c * K + g * 8;
-    // four steps of loads in flight before their MFMAs (steps past s1 are
-    // clamped to s1 - 1 and their products skipped)
-    for (int64_t st = s0; st < s1; st += 4) {
-        bf16x8 xf[4], af[4][NB];
+    // U steps of loads in flight before their MFMAs.  A step past s1 reloads
+    // step s1 - 1 with its X fragment zeroed, so it adds exact zeros: the
+    // loop has no branch for the compiler to sink the loads into.
+    const bf16x8 zero = {};
+    for (int64_t st = s0; st < s1; st += U) {
+        bf16x8 xf[U][ROWT], af[U][NB];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int64_t su = st + u < s1 ? st + u : s1 - 1;
-            xf[u] = *(const bf16x8 *)(xp + su * 32);
+        for (int u = 0; u < U; ++u) {
+            const bool ok = st + u < s1;  // wave-uniform
+            const int64_t su = ok ? st + u : s1 - 1;
+#pragma unroll
+            for (int t = 0; t < ROWT; ++t) {
+                const bf16x8 v = *(const bf16x8 *)(xp[t] + su * 32);
+                xf[u][t] = ok ? v : zero;
+            }
 #pragma unroll
             for (int j = 0; j < NB; ++j) af[u][j] = *(const bf16x8 *)(ap + (int64_t)j * 16 * K + su * 32);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (st + u >= s1) break;
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int j = 0; j < NB; ++j)
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[u], af[u][j], acc[j], 0, 0, 0);
-        }
+            for (int t = 0; t < ROWT; ++t)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[u][t], af[u][j],
+                                                                        acc[t][j], 0, 0, 0);
     }
 #pragma unroll
-    for (int j = 0; j < NB; ++j) part[wave][j][lane] = acc[j];
+    for (int t = 0; t < ROWT; ++t)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) part[wave][t][j][lane] = acc[t][j];
     __syncthreads();
     if (wave != 0) return;
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-        const f32x4 v = ((part[0][j][lane] + part[1][j][lane]) + part[2][j][lane]) + part[3][j][lane];
+    for (int t = 0; t < ROWT; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int64_t row = m0 + g * 4 + e;
-            if (row < M) ((__bf16 *)XA)[row * r + j * 16 + c] = (__bf16)v[e];
+        for (int j = 0; j < NB; ++j) {
+            const f32x4 v = ((part[0][t][j][lane] + part[1][t][j][lane]) + part[2][t][j][lane]) +
+                            part[3][t][j][lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t row = m0 + t * 16 + g * 4 + e;
+                if (row < M) ((__bf16 *)XA)[row * r + j * 16 + c] = (__bf16)v[e];
+            }
         }
-    }
 }
 
 hipError_t launch_lora_down(const uint16_t *x, const uint16_t *a, int64_t M, int64_t K, int64_t r,
                             uint16_t *xa, hipStream_t s) {
     if (M == 0) return hipSuccess;
-    const dim3 grid((unsigned)((M + 15) / 16));
-#define NVFP4_LD(NB) \
-    NVFP4_LAUNCH("lora_down", lora_down_kernel<NB>, grid, dim3(256), 0, s, x, a, M, K, xa)
+    // two 16-row tiles per workgroup (measured against one and four); ROWT x NB
+    // <= 16 bounds the LDS hand-off at 64 KB
+    constexpr int kRowTiles = 2;
+#define NVFP4_LD(NB)                                                                        \
+    {                                                                                       \
+        constexpr int RT = kRowTiles * (NB) <= 16 ? kRowTiles : 16 / (NB);                   \
+        const dim3 grid((unsigned)((M + 16 * RT - 1) / (16 * RT)));                          \
+        NVFP4_LAUNCH("lora_down", (lora_down_kernel<NB, RT>), grid, dim3(256), 0, s, x, a, M, \
+                     K, xa);                                                                \
+    }
     switch (r) {
     case 16: NVFP4_LD(1); break;
     case 32: NVFP4_LD(2); break;

@@ -112,6 +112,32 @@ def test_gemm_attention_projection_sampled(nv, orc):
     check(nv, orc, qa, qw, torch.bfloat16, rows=rows)
 
 
+@pytest.mark.parametrize("N,K", [(14336, 3072), (3072, 14336)], ids=["ffn_up", "ffn_down"])
+def test_gemm_ffn_shapes_sampled(nv, orc, N, K):
+    """The FFN projections at full size (M = 7040): the GPU quantizes the whole
+    bf16 activation, the oracle quantizes the sampled rows with the exact
+    tensor amax (1-D blocks are independent once the tensor scale is fixed)
+    and takes the fp64 product with the oracle-quantized weight."""
+    print("case: gemm ffn", 7040, N, K, flush=True)
+    M = 7040
+    A = synth.bf16_bits_to_f32(synth.to_bf16_bits(synth.activations(1004, 0, M, K, 0.005, 30.0)))
+    W = synth.weights(1004, 1 if N > K else 2, N, K)
+    qw = orc.quantize(W, layout=orc.LAYOUT_2D)
+    rows = np.unique(np.concatenate([[0, 255, 6912, M - 1],
+                                     np.random.default_rng(2).integers(0, M, 28)]))
+    qa_rows = orc.quantize(A[rows], amax=float(np.abs(A).max()))
+    a = nv.quantize(torch.from_numpy(A).cuda().to(torch.bfloat16))
+    w = upload(nv, *qw, 1)
+    y = nv.gemm_w4a4(a, w, out_dtype=torch.bfloat16)
+    yr, bound = orc.gemm_ref(*qa_rows, *qw)
+    torch.cuda.synchronize()
+    yg = y[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+    tol = 1e-5 * bound + 2.0 ** -8 * np.abs(yr)
+    err = np.abs(yg - yr)
+    worst = np.unravel_index(np.argmax(err - tol), err.shape)
+    assert np.all(err <= tol), f"max excess at {worst}: err {err[worst]} tol {tol[worst]}"
+
+
 def test_gemm_deterministic(nv, orc):
     qa, qw = operands(orc, 512, 384, 1024, 1007)
     a = upload(nv, *qa, 0)
