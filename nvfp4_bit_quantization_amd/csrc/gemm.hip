@@ -41,6 +41,7 @@
 // from registers, expanding each fragment dword just before its MFMAs.
 // Other K: the same MFMA schedule from per-lane loads straight from memory,
 // with blocks past K read as zero.
+#include <atomic>
 #include <utility>
 
 #include "device.hpp"
@@ -450,6 +451,24 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
     }
 }
 
+// Raise the dynamic-LDS limit of `fns` to `bytes` once per device: `done`
+// holds one bit per device id (0..31) already set up.  Threads that race
+// both set the attribute, which is harmless.
+static hipError_t lds_limit_once(const void *const *fns, int n, int bytes,
+                                 std::atomic<uint32_t> &done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint32_t bit = (dev >= 0 && dev < 32) ? (1u << dev) : 0u;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    for (int i = 0; i < n; ++i) {
+        e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        if (e != hipSuccess) return e;
+    }
+    done.fetch_or(bit, std::memory_order_release);
+    return hipSuccess;
+}
+
 hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_sdec,
                             const uint8_t *w_codes, const uint8_t *w_scales,
                             const float *w_sdec, int64_t M, int64_t N, int64_t K, int w_layout,
@@ -465,23 +484,17 @@ hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, con
     // LDS path: K a multiple of the step, and buffer offsets that fit 31 bits
     const bool fast = K % BK == 0 && M * (K / 2) < ((int64_t)1 << 31) &&
                       N * (K / 2) < ((int64_t)1 << 31);
-    static bool attr_set = false;
-    if (!attr_set) {
-        const void *fns[8] = {(const void *)gemm_w4a4_kernel<true, true, true, false>,
-                              (const void *)gemm_w4a4_kernel<false, true, true, false>,
-                              (const void *)gemm_w4a4_kernel<true, true, false, false>,
-                              (const void *)gemm_w4a4_kernel<false, true, false, false>,
-                              (const void *)gemm_w4a4_kernel<true, true, true, true>,
-                              (const void *)gemm_w4a4_kernel<false, true, true, true>,
-                              (const void *)gemm_w4a4_kernel<true, true, false, true>,
-                              (const void *)gemm_w4a4_kernel<false, true, false, true>};
-        for (const void *f : fns) {
-            hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               kLdsBytes);
-            if (e != hipSuccess) return e;
-        }
-        attr_set = true;
-    }
+    static std::atomic<uint32_t> lds_set{0};
+    const void *fns[8] = {(const void *)gemm_w4a4_kernel<true, true, true, false>,
+                          (const void *)gemm_w4a4_kernel<false, true, true, false>,
+                          (const void *)gemm_w4a4_kernel<true, true, false, false>,
+                          (const void *)gemm_w4a4_kernel<false, true, false, false>,
+                          (const void *)gemm_w4a4_kernel<true, true, true, true>,
+                          (const void *)gemm_w4a4_kernel<false, true, true, true>,
+                          (const void *)gemm_w4a4_kernel<true, true, false, true>,
+                          (const void *)gemm_w4a4_kernel<false, true, false, true>};
+    hipError_t e = lds_limit_once(fns, 8, kLdsBytes, lds_set);
+    if (e != hipSuccess) return e;
 #define NVFP4_GEMM(BF, KF, W2, LO)                                                            \
     NVFP4_LAUNCH(LO ? "gemm_w4a4_lora" : "gemm_w4a4", (gemm_w4a4_kernel<BF, KF, W2, LO>), grid, \
                  dim3(256), KF ? kLdsBytes : 0, s, g, a_sdec, w_sdec, y, amax_out, la)
@@ -754,16 +767,10 @@ hipError_t launch_gemm_mx(const uint8_t *a_codes, const uint8_t *a_scales, const
                           const uint8_t *w_scales, int64_t M, int64_t N, int64_t K, void *y,
                           int ydtype, hipStream_t s) {
     if (M == 0 || N == 0) return hipSuccess;
-    static bool attr_set = false;
-    if (!attr_set) {
-        const void *fns[2] = {(const void *)gemm_mx_kernel<true>, (const void *)gemm_mx_kernel<false>};
-        for (const void *f : fns) {
-            hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               kLdsBytes);
-            if (e != hipSuccess) return e;
-        }
-        attr_set = true;
-    }
+    static std::atomic<uint32_t> lds_set{0};
+    const void *fns[2] = {(const void *)gemm_mx_kernel<true>, (const void *)gemm_mx_kernel<false>};
+    hipError_t e = lds_limit_once(fns, 2, kLdsBytes, lds_set);
+    if (e != hipSuccess) return e;
     const int64_t ntiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const GemmArgs g{a_codes, a_scales, w_codes, w_scales, M, N, K};
     if (ydtype == kBF16)
