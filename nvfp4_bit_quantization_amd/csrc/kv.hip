@@ -40,7 +40,8 @@ constexpr int kSeq = 16;            // tokens summed sequentially by one lane
 constexpr int kStatsTokens = 64;    // tokens per stats unit (4 tiles of 16)
 constexpr int kGroupCh = 512;       // channels per stats unit (64 lanes x 8)
 constexpr int kFinCh = 16;          // channels per finalize wave
-constexpr int64_t kEncodeGrid = 512; // encode workgroups per tensor (upper bound)
+constexpr int64_t kEncodeGrid = 4096; // encode workgroups per tensor (upper bound)
+constexpr int64_t kEncodeBlocks = 6;  // target blocks per encode lane (measured: 6 over ~10)
 
 struct KvWs {
     double *P;      // [nt64, HD]  level-2 tree nodes (64-token sums)
@@ -484,10 +485,11 @@ hipError_t launch_kv_store(const KvStoreArgs &a, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nblk = a.T * a.HD / 16;
-    // Grid: up to kEncodeGrid workgroups per tensor.  If a multiple of
-    // m = NB / gcd(NB, 256) fits (NB = blocks per token), the grid is that
-    // multiple, so the stride in blocks is a multiple of NB.
-    int64_t g = (nblk + 255) / 256;
+    // Grid: about kEncodeBlocks blocks per lane (whole iterations of the
+    // three-block loop), at most kEncodeGrid workgroups per tensor.  If a
+    // multiple of m = NB / gcd(NB, 256) fits (NB = blocks per token), the grid
+    // is the next such multiple, so the stride in blocks is a multiple of NB.
+    int64_t g = (nblk + 256 * kEncodeBlocks - 1) / (256 * kEncodeBlocks);
     if (g > kEncodeGrid) g = kEncodeGrid;
     if (g < 1) g = 1;
     const int64_t NB = a.HD / 16;
@@ -498,7 +500,7 @@ hipError_t launch_kv_store(const KvStoreArgs &a, hipStream_t s) {
     }
     bool fixed = false;
     if (gc <= g) {
-        g = (g / gc) * gc;
+        g = ((g + gc - 1) / gc) * gc;
         fixed = true;
     } else if (gc <= 2 * kEncodeGrid) {
         g = gc;
