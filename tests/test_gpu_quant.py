@@ -140,3 +140,24 @@ def test_quantize_full_size_activation_sampled(nv, orc):
     assert q.s_dec == d_ref
     assert np.array_equal(q.codes.cpu().numpy()[rows], c_ref)
     assert np.array_equal(q.scales.cpu().numpy()[rows], s_ref)
+
+
+def test_quantize_1d_fp32_past_2gib_sampled(nv, orc):
+    """fp32 input of 2^29 + 524288 elements (2.15 GB): past the 2^31-byte
+    limit of the buffer-offset encoder, so the pointer path runs.  The tensor
+    scale comes from the whole input; codes and scales of 64 sampled rows
+    (first and last included) against the oracle."""
+    rows_n, cols = (1 << 20) + 1024, 512
+    print("case: 1-D fp32", rows_n, "x", cols, flush=True)
+    x = np.random.default_rng(1008).standard_normal((rows_n, cols), dtype=np.float32)
+    x[7, :16] *= 50.0  # one outlier block sets the tensor scale
+    q = nv.quantize(torch.from_numpy(x).cuda())
+    amax = float(orc.amax(x))
+    rows = np.unique(np.concatenate([[0, 7, rows_n - 1],
+                                     np.random.default_rng(9).integers(0, rows_n, 61)]))
+    c_ref, s_ref, d_ref = orc.quantize(x[rows], amax=amax)
+    torch.cuda.synchronize()
+    assert q.s_dec == d_ref
+    idx = torch.from_numpy(rows).cuda()
+    assert np.array_equal(q.codes[idx].cpu().numpy(), c_ref)
+    assert np.array_equal(q.scales[idx].cpu().numpy(), s_ref)
