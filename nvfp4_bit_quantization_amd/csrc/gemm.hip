@@ -33,9 +33,11 @@
 // per row, scales 16 bytes per row or 16-row group) go from memory straight
 // to LDS (global_load_lds, 16 bytes per lane, 8 lanes per 128-byte row, so
 // every load instruction covers 8 whole cache lines), two LDS stages.  The
-// 16-byte columns of each 8-row block are XOR-swizzled by the row (column c
-// of row r sits in slot c ^ (r & 7)), so the fragment reads -- 8 rows per
-// column -- hit 8 different bank groups.  Per K step: barrier; each wave
+// 16-byte columns of each row are XOR-swizzled by the row (column c of tile
+// row r sits in slot c ^ ((r >> 1) & 7)): a fragment read takes one column
+// of 16 consecutive rows per 16 lanes, and those 16 slots -- two rows of
+// 128 bytes per 256 bytes of LDS -- land in 16 different groups of the 64
+// banks, so the reads run without bank conflicts.  Per K step: barrier; each wave
 // reads its whole step of fragments from LDS into registers; the loads of
 // the next step are issued into the other stage; the 16 MFMA substeps run
 // from registers, expanding each fragment dword just before its MFMAs.
@@ -178,8 +180,8 @@ __device__ __forceinline__ void substep(f32x16 (&acc)[FM][FN], const Frag (&A)[F
 // Buffer descriptors over the four packed arrays and this lane's byte
 // offsets into them for its share of every step's direct-to-LDS loads:
 // A code blocks 8w .. 8w + 7 and W code blocks 6w .. 6w + 5 of the tile
-// (8 rows each; lane j loads 16-byte column (j & 7) ^ (j >> 3) of row
-// j >> 3 into slot j), the A scales of tile rows 64w + j, and (wave 0, lanes
+// (8 rows each; lane j loads 16-byte column (j & 7) ^ ((R >> 1) & 7) of
+// tile row R = 8 * block + (j >> 3) into slot j), the A scales of tile rows 64w + j, and (wave 0, lanes
 // below 12) the W scales of the tile's 16-row groups.  Rows past the matrix
 // edge are clamped to the last row.  The step's offset is a scalar added at
 // each load.  (The host sends matrices of 2^31 bytes or more to the general
@@ -204,17 +206,22 @@ __device__ __forceinline__ void stage_src(StageSrc &q, const GemmArgs &g, int64_
                                                  (int)((W2D ? g.N >> 4 : g.N) * KB),
                                                  kBufferWord3);
     }
-    const int rib = lane >> 3, gcol = (lane & 7) ^ rib;
+    // block parity gives bit 2 of the swizzle key (8 rows per block; both
+    // per-wave block counts are even)
+    static_assert((BM / 32) % 2 == 0 && (BN / 32) % 2 == 0, "block parity");
+    const int rib = lane >> 3;
 #pragma unroll
     for (int bb = 0; bb < BM / 32; ++bb) {
         const int64_t row0 = m0 + (wave * (BM / 32) + bb) * 8 + rib;
         const int64_t row = row0 < g.M ? row0 : g.M - 1;
+        const int gcol = (lane & 7) ^ ((bb & 1) << 2 | rib >> 1);
         q.a[bb] = (uint32_t)(row * kbytes) + gcol * 16;
     }
 #pragma unroll
     for (int bb = 0; bb < BN / 32; ++bb) {
         const int64_t row0 = n0 + (wave * (BN / 32) + bb) * 8 + rib;
         const int64_t row = row0 < g.N ? row0 : g.N - 1;
+        const int gcol = (lane & 7) ^ ((bb & 1) << 2 | rib >> 1);
         q.w[bb] = (uint32_t)(row * kbytes) + gcol * 16;
     }
     const int64_t ar0 = m0 + wave * 64 + lane;
@@ -257,11 +264,12 @@ __device__ __forceinline__ void stage_load(const StageSrc &q, uint8_t *stage, in
 
 // The wave's fragments of one K step from LDS: lane (r, h) reads, for each
 // fragment row R, the 16-byte columns 4h .. 4h + 3 (un-swizzled) and the 8
-// scale bytes of its half.
+// scale bytes of its half.  Fragments start on multiples of 32 tile rows, so
+// the swizzle key of row R is (r >> 1) & 7.
 template <bool SCALES, bool W2D>
 __device__ __forceinline__ void stage_read(Frag (&A)[FM], Frag (&B)[FN], const uint8_t *stage,
                                            int wm, int wn, int r, int h) {
-    const int rib = r & 7;
+    const int rib = r & 7, key = (r >> 1) & 7;
     if (SCALES) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -274,7 +282,7 @@ __device__ __forceinline__ void stage_read(Frag (&A)[FM], Frag (&B)[FN], const u
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        const int slot = ((h * 4 + c) ^ rib) * 16 + rib * 128;
+        const int slot = ((h * 4 + c) ^ key) * 16 + rib * 128;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
             A[i].q[c] = *(const u32x4 *)(stage + kAOff + ((wm * WM + i * 32 + r) >> 3) * 1024 + slot);
