@@ -166,6 +166,27 @@ int nvfp4_gemm_w4a4(const nvfp4_tensor *a, const nvfp4_tensor *w, void *y, int32
                     float *amax_out, void *stream);
 
 /*
+ * W4A4 GEMM whose epilogue writes NVFP4 directly (producer-fused
+ * requantization; TX page, NVFP4 section: the NVFP4 inference path gained
+ * fused kernels and in-place quantization updates; DR summary, inference
+ * infrastructure: the activations feeding the next FP4 GEMM are 1-D NVFP4).
+ * y (1-D layout, [M, N], caller-owned codes / scales / s_dec) receives
+ *   nvfp4_quantize(bf16(Y), search, amax_in)
+ * bit for bit, Y the nvfp4_gemm_w4a4 product (bf16 nearest-even), so the
+ * next GEMM reads 0.5625 bytes an element instead of a bf16 Y written and
+ * read back.  amax_in (device fp32, required) is the tensor amax the encode
+ * uses: max|bf16(Y)| gives exactly the unfused result; any other value (an
+ * amax from an earlier call, a calibrated one) is used as given, values
+ * beyond it saturating as in nvfp4_quantize (block scale 448, codes 6).
+ * amax_out: NULL, or raised to max|bf16(Y)| as in nvfp4_gemm_w4a4 (the
+ * amax the next call may use).  Shapes and layouts of a and w as
+ * nvfp4_gemm_w4a4; y->rows == M, y->cols == N.  M == 0 or N == 0 writes
+ * s_dec only.
+ */
+int nvfp4_gemm_w4a4_quant(const nvfp4_tensor *a, const nvfp4_tensor *w, const nvfp4_tensor *y,
+                          int32_t search, const float *amax_in, float *amax_out, void *stream);
+
+/*
  * LoRA on the frozen NVFP4 backbone (DR few-step distillation: the model is
  * the frozen quantized backbone plus LoRA adapters, W ~ Dequant(Q_search(W_0))
  * + (alpha/r) B A; IT: only the LoRA adapters are trained on the frozen

@@ -74,6 +74,8 @@ _EXPORTS = {
                             C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p], C.c_int),
     "nvfp4_gemm_w4a4": ([C.POINTER(CTensor), C.POINTER(CTensor), C.c_void_p, C.c_int32,
                          C.c_void_p, C.c_void_p], C.c_int),
+    "nvfp4_gemm_w4a4_quant": ([C.POINTER(CTensor), C.POINTER(CTensor), C.POINTER(CTensor),
+                               C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p], C.c_int),
     "nvfp4_lora_down": ([C.c_void_p, C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p,
                          C.c_void_p], C.c_int),
     "nvfp4_gemm_w4a4_lora": ([C.POINTER(CTensor), C.POINTER(CTensor), C.c_void_p, C.c_void_p,
@@ -252,6 +254,29 @@ def gemm_w4a4(a: NVFP4Tensor, w: NVFP4Tensor, out_dtype=torch.bfloat16,
     _check(lib().nvfp4_gemm_w4a4(C.byref(ca), C.byref(cw), _dev(out, "out"), _DT[out.dtype],
                                  None if amax_out is None else amax_out.data_ptr(),
                                  _stream(stream)))
+    return out
+
+
+def _amax_arg(t, name):
+    if t is not None and (t.dtype != torch.float32 or t.numel() != 1 or not t.is_cuda):
+        raise ValueError(f"{name} must be a one-element float32 device tensor")
+    return None if t is None else t.data_ptr()
+
+
+def gemm_w4a4_quant(a: NVFP4Tensor, w: NVFP4Tensor, amax_in: torch.Tensor,
+                    search: int = SEARCH_4O6, out: NVFP4Tensor | None = None,
+                    amax_out: torch.Tensor | None = None, stream=None) -> NVFP4Tensor:
+    """nvfp4_gemm_w4a4_quant: the W4A4 product encoded by the GEMM's epilogue
+    to a 1-D NVFP4Tensor [M, N], with the tensor amax taken from amax_in (a
+    one-element float32 device tensor).  amax_out as in gemm_w4a4."""
+    if out is None:
+        out = NVFP4Tensor.empty(a.rows, w.rows, LAYOUT_1D, a.codes.device)
+    if amax_in is None:
+        raise ValueError("gemm_w4a4_quant needs amax_in")
+    pin, pout = _amax_arg(amax_in, "amax_in"), _amax_arg(amax_out, "amax_out")
+    ca, cw, cy = a.c(), w.c(), out.c()
+    _check(lib().nvfp4_gemm_w4a4_quant(C.byref(ca), C.byref(cw), C.byref(cy), search, pin, pout,
+                                       _stream(stream)))
     return out
 
 

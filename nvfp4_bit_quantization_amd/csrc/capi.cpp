@@ -285,8 +285,32 @@ int nvfp4_gemm_w4a4(const nvfp4_tensor *a, const nvfp4_tensor *w, void *y, int32
     hipError_t e = nvfp4::launch_gemm_w4a4(a->codes, a->scales, a->s_dec, w->codes, w->scales,
                                            w->s_dec, a->rows, w->rows, a->cols, w->layout, y,
                                            y_dtype, amax_out, nullptr, nullptr, 0, 0.0f,
-                                           (hipStream_t)stream);
+                                           nullptr, (hipStream_t)stream);
     return hip_status(e, "gemm launch");
+}
+
+int nvfp4_gemm_w4a4_quant(const nvfp4_tensor *a, const nvfp4_tensor *w, const nvfp4_tensor *y,
+                          int32_t search, const float *amax_in, float *amax_out, void *stream) {
+    int st = check_tensor(y, "gemm_quant Y");
+    if (st) return st;
+    if (y->layout != NVFP4_LAYOUT_1D)
+        return fail(NVFP4_EINVAL, "gemm_quant: Y must use 1-D (1x16) block scaling");
+    st = check_gemm(a, w, y->codes, NVFP4_DTYPE_BF16, amax_out);
+    if (st) return st;
+    if (y->rows != a->rows || y->cols != w->rows)
+        return fail(NVFP4_ESHAPE, "gemm_quant: Y is [%lld, %lld], the product [%lld, %lld]",
+                    (long long)y->rows, (long long)y->cols, (long long)a->rows,
+                    (long long)w->rows);
+    if (search != NVFP4_SEARCH_6 && search != NVFP4_SEARCH_4O6)
+        return fail(NVFP4_EINVAL, "gemm_quant: bad search %d", search);
+    if (!amax_in) return fail(NVFP4_EINVAL, "gemm_quant: NULL amax_in");
+    if (((uintptr_t)amax_in & 3u)) return fail(NVFP4_EALIGN, "gemm_quant: amax_in misaligned");
+    const nvfp4::QuantOut q{y->codes, y->scales, y->s_dec, amax_in, search == NVFP4_SEARCH_4O6};
+    hipError_t e = nvfp4::launch_gemm_w4a4(a->codes, a->scales, a->s_dec, w->codes, w->scales,
+                                           w->s_dec, a->rows, w->rows, a->cols, w->layout,
+                                           nullptr, NVFP4_DTYPE_BF16, amax_out, nullptr, nullptr,
+                                           0, 0.0f, &q, (hipStream_t)stream);
+    return hip_status(e, "gemm_quant launch");
 }
 
 int nvfp4_gemm_w4a4_lora(const nvfp4_tensor *a, const nvfp4_tensor *w, const void *xa_bf16,
@@ -302,7 +326,7 @@ int nvfp4_gemm_w4a4_lora(const nvfp4_tensor *a, const nvfp4_tensor *w, const voi
     hipError_t e = nvfp4::launch_gemm_w4a4(
         a->codes, a->scales, a->s_dec, w->codes, w->scales, w->s_dec, a->rows, w->rows, a->cols,
         w->layout, y, y_dtype, amax_out, (const uint16_t *)xa_bf16, (const uint16_t *)b_bf16, r,
-        lora_scale, (hipStream_t)stream);
+        lora_scale, nullptr, (hipStream_t)stream);
     return hip_status(e, "gemm_lora launch");
 }
 

@@ -14,6 +14,10 @@
 //   [2^-10, 2688]: exact in fp16).
 // The FP32 tensor scales are applied once in the epilogue:
 //   Y = RN(RN(s_A * s_W) * acc), acc the fp32 MFMA accumulation.
+// With QUANT the epilogue encodes bf16(Y) straight to NVFP4 (1-D blocks
+// along N, the Four-Over-Six encoder of the quantizer) for a tensor amax the
+// caller gives, so the next W4A4 GEMM reads it without a bf16 round trip
+// through memory.
 //
 // Operand layout in the MFMA: the 32x32x16 MFMA pairs lane l's 8 K values
 // of row (l & 31) with the same 8 K positions of the other operand, and the
@@ -307,12 +311,23 @@ struct LoraArgs {
     float scale;
 };
 
-template <bool OUT_BF16, bool KFAST, bool W2D, bool LORA>
+// Per-wave LDS of the fused epilogue: the wave's 128 x 96 tile of bf16(Y)
+// (row-major, 192 bytes a row), then the (S, 1/S) table of the 128
+// non-negative scale codes for the tensor's s_dec.
+constexpr int kQRowBytes = WN * 2;
+constexpr int kQTileBytes = WM * kQRowBytes;           // 24576
+constexpr int kQLutOff = kQTileBytes;
+constexpr int kQWaveBytes = kQTileBytes + 128 * 8;     // 25600
+static_assert(4 * kQWaveBytes <= kLdsBytes, "fused-encode LDS");
+
+template <bool OUT_BF16, bool KFAST, bool W2D, bool LORA, bool QUANT>
 __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float *__restrict__ a_sdec,
                                                         const float *__restrict__ w_sdec,
                                                         void *__restrict__ yv,
-                                                        float *__restrict__ amax_out, LoraArgs la) {
+                                                        float *__restrict__ amax_out, LoraArgs la,
+                                                        QuantOut qo) {
     const int64_t M = g.M, N = g.N, K = g.K;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int64_t tn_count = (N + BN - 1) / BN;
     const int64_t ntiles = ((M + BM - 1) / BM) * tn_count;
     // XCD-aware tile order: workgroup b runs on XCD b % 8; XCD x takes the
@@ -342,7 +357,6 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
     const int64_t nk = (K + BK - 1) / BK;
     Frag A[FM], B[FN];
     if (KFAST) {
-        extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
         StageSrc src;
         stage_src<true, W2D>(src, g, m0, n0, wave, lane);
         stage_load<true, W2D>(src, lds, 0, wave, lane);
@@ -370,6 +384,8 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
         }
         // no load into LDS is still in flight when the wave leaves
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // the fused encode reuses the stages: every wave is past its last read
+        if (QUANT) __syncthreads();
     } else if (active) {
         FragPtr pa[FM], pb[FN];
 #pragma unroll
@@ -386,10 +402,16 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
             step_all(acc, A, B, std::make_integer_sequence<int, NSUB>{});
         }
     }
+    if (QUANT && blockIdx.x == 0 && threadIdx.x == 0) {
+        float s_enc, s_dec;
+        tensor_scales(*qo.amax_in, s_enc, s_dec);
+        *qo.s_dec = s_dec;
+    }
     if (!active) return;
 
     const float scale = (*a_sdec) * (*w_sdec);
     float amax = 0.0f;  // max |stored y| of this lane
+    uint8_t *const qw = lds + wave * kQWaveBytes;  // QUANT: this wave's tile and table
     // LoRA: (XA rows of block i) x (B rows of block j)^T on the bf16 MFMA, 16
     // of r per step, for two row blocks x three column blocks at a time; each
     // step loads those 2 + 3 fragments at once (rows past the edge are
@@ -440,7 +462,12 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
                     const int64_t row = rbase + (e >> 2) * 8 + (e & 3);
                     float v = scale * acc[i][j][e];
                     if (LORA) v = __builtin_fmaf(la.scale, lo[ii][j][e], v);
-                    if (row < M && col < N) {
+                    if (QUANT) {
+                        const __bf16 b = (__bf16)v;
+                        if (row < M && col < N) amax = fmaxf(amax, fabsf((float)b));
+                        const int rl = i * 32 + h * 4 + (e >> 2) * 8 + (e & 3);
+                        *(__bf16 *)(qw + rl * kQRowBytes + (j * 32 + r) * 2) = b;
+                    } else if (row < M && col < N) {
                         if (OUT_BF16) {
                             const __bf16 b = (__bf16)v;
                             ((__bf16 *)yv)[row * N + col] = b;
@@ -452,6 +479,40 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
                     }
                 }
             }
+    }
+    if (QUANT) {
+        // 1x16 blocks of the wave's tile, 12 per lane: bf16 values back from
+        // LDS, the quantizer's Four-Over-Six encode (same table, same
+        // operation order), codes and scale byte to Y.  Only this wave
+        // touches its region; the wait (also a compiler barrier) puts every
+        // table and tile write before the reads of other lanes' values.
+        float s_enc, s_dec;
+        tensor_scales(*qo.amax_in, s_enc, s_dec);
+        f32x2 *const lut = (f32x2 *)(qw + kQLutOff);
+        lut[lane] = scale_entry(lane, s_dec);
+        lut[lane + 64] = scale_entry(lane + 64, s_dec);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        constexpr int kBlkRow = WN / 16;  // 6 blocks a row
+#pragma unroll 2
+        for (int k = 0; k < WM * kBlkRow / 64; ++k) {
+            const int blk = lane + 64 * k;
+            const int rl = blk / kBlkRow, cb = blk - rl * kBlkRow;
+            const int64_t row = mw + rl, col = nw + cb * 16;
+            Raw16Bf16 raw;
+            raw.a = *(const u32x4 *)(qw + rl * kQRowBytes + cb * 32);
+            raw.b = *(const u32x4 *)(qw + rl * kQRowBytes + cb * 32 + 16);
+            float x[16];
+            unpack16(raw, x);
+            uint32_t q_lo, q_hi, sc;
+            if (qo.four_over_six)
+                encode_block16<true>(x, s_enc, lut, q_lo, q_hi, sc);
+            else
+                encode_block16<false>(x, s_enc, lut, q_lo, q_hi, sc);
+            if (row < M && col < N) {
+                *(u32x2 *)(qo.codes + row * (N >> 1) + (col >> 1)) = u32x2{q_lo, q_hi};
+                qo.scales[row * (N >> 4) + (col >> 4)] = (uint8_t)sc;
+            }
+        }
     }
     if (amax_out) {
         amax = wave_max(amax);
@@ -477,57 +538,80 @@ static hipError_t lds_limit_once(const void *const *fns, int n, int bytes,
     return hipSuccess;
 }
 
+// s_dec of an empty fused-encode output.
+__global__ void quant_sdec_kernel(const float *__restrict__ amax_in, float *__restrict__ s_dec) {
+    if (threadIdx.x == 0) {
+        float s_enc, sd;
+        tensor_scales(*amax_in, s_enc, sd);
+        *s_dec = sd;
+    }
+}
+
 hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_sdec,
                             const uint8_t *w_codes, const uint8_t *w_scales,
                             const float *w_sdec, int64_t M, int64_t N, int64_t K, int w_layout,
                             void *y, int ydtype, float *amax_out, const uint16_t *lora_xa,
                             const uint16_t *lora_b, int64_t lora_r, float lora_scale,
-                            hipStream_t s) {
-    if (M == 0 || N == 0) return hipSuccess;
+                            const QuantOut *quant, hipStream_t s) {
+    if (M == 0 || N == 0) {
+        if (!quant) return hipSuccess;
+        NVFP4_LAUNCH("gemm_w4a4_quant", quant_sdec_kernel, dim3(1), dim3(64), 0, s,
+                     quant->amax_in, quant->s_dec);
+        return hipGetLastError();
+    }
     const int64_t ntiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const dim3 grid((unsigned)ntiles);
     const GemmArgs g{a_codes, a_scales, w_codes, w_scales, M, N, K};
     const LoraArgs la{lora_xa, lora_b, lora_r, lora_scale};
+    const QuantOut qo = quant ? *quant : QuantOut{};
     const bool lora = lora_xa != nullptr;
     // LDS path: K a multiple of the step, and buffer offsets that fit 31 bits
     const bool fast = K % BK == 0 && M * (K / 2) < ((int64_t)1 << 31) &&
                       N * (K / 2) < ((int64_t)1 << 31);
     static std::atomic<uint32_t> lds_set{0};
-    const void *fns[8] = {(const void *)gemm_w4a4_kernel<true, true, true, false>,
-                          (const void *)gemm_w4a4_kernel<false, true, true, false>,
-                          (const void *)gemm_w4a4_kernel<true, true, false, false>,
-                          (const void *)gemm_w4a4_kernel<false, true, false, false>,
-                          (const void *)gemm_w4a4_kernel<true, true, true, true>,
-                          (const void *)gemm_w4a4_kernel<false, true, true, true>,
-                          (const void *)gemm_w4a4_kernel<true, true, false, true>,
-                          (const void *)gemm_w4a4_kernel<false, true, false, true>};
-    hipError_t e = lds_limit_once(fns, 8, kLdsBytes, lds_set);
+    const void *fns[12] = {(const void *)gemm_w4a4_kernel<true, true, true, false, false>,
+                           (const void *)gemm_w4a4_kernel<false, true, true, false, false>,
+                           (const void *)gemm_w4a4_kernel<true, true, false, false, false>,
+                           (const void *)gemm_w4a4_kernel<false, true, false, false, false>,
+                           (const void *)gemm_w4a4_kernel<true, true, true, true, false>,
+                           (const void *)gemm_w4a4_kernel<false, true, true, true, false>,
+                           (const void *)gemm_w4a4_kernel<true, true, false, true, false>,
+                           (const void *)gemm_w4a4_kernel<false, true, false, true, false>,
+                           (const void *)gemm_w4a4_kernel<true, true, true, false, true>,
+                           (const void *)gemm_w4a4_kernel<true, true, false, false, true>,
+                           (const void *)gemm_w4a4_kernel<true, false, true, false, true>,
+                           (const void *)gemm_w4a4_kernel<true, false, false, false, true>};
+    hipError_t e = lds_limit_once(fns, 12, kLdsBytes, lds_set);
     if (e != hipSuccess) return e;
-#define NVFP4_GEMM(BF, KF, W2, LO)                                                            \
-    NVFP4_LAUNCH(LO ? "gemm_w4a4_lora" : "gemm_w4a4", (gemm_w4a4_kernel<BF, KF, W2, LO>), grid, \
-                 dim3(256), KF ? kLdsBytes : 0, s, g, a_sdec, w_sdec, y, amax_out, la)
-#define NVFP4_GEMM_K(BF, W2, LO)     \
-    if (fast)                        \
-        NVFP4_GEMM(BF, true, W2, LO); \
-    else                             \
-        NVFP4_GEMM(BF, false, W2, LO);
-#define NVFP4_GEMM_W(BF, LO)             \
+#define NVFP4_GEMM(BF, KF, W2, LO, Q)                                                       \
+    NVFP4_LAUNCH(Q ? "gemm_w4a4_quant" : LO ? "gemm_w4a4_lora" : "gemm_w4a4",                \
+                 (gemm_w4a4_kernel<BF, KF, W2, LO, Q>), grid, dim3(256),                      \
+                 KF ? kLdsBytes : Q ? 4 * kQWaveBytes : 0, s, g, a_sdec, w_sdec, y, amax_out, \
+                 la, qo)
+#define NVFP4_GEMM_K(BF, W2, LO, Q)      \
+    if (fast)                            \
+        NVFP4_GEMM(BF, true, W2, LO, Q); \
+    else                                 \
+        NVFP4_GEMM(BF, false, W2, LO, Q);
+#define NVFP4_GEMM_W(BF, LO, Q)          \
     if (w_layout) {                      \
-        NVFP4_GEMM_K(BF, true, LO)       \
+        NVFP4_GEMM_K(BF, true, LO, Q)    \
     } else {                             \
-        NVFP4_GEMM_K(BF, false, LO)      \
+        NVFP4_GEMM_K(BF, false, LO, Q)   \
     }
-    if (ydtype == kBF16) {
+    if (quant) {
+        NVFP4_GEMM_W(true, false, true)
+    } else if (ydtype == kBF16) {
         if (lora) {
-            NVFP4_GEMM_W(true, true)
+            NVFP4_GEMM_W(true, true, false)
         } else {
-            NVFP4_GEMM_W(true, false)
+            NVFP4_GEMM_W(true, false, false)
         }
     } else {
         if (lora) {
-            NVFP4_GEMM_W(false, true)
+            NVFP4_GEMM_W(false, true, false)
         } else {
-            NVFP4_GEMM_W(false, false)
+            NVFP4_GEMM_W(false, false, false)
         }
     }
 #undef NVFP4_GEMM_W

@@ -89,12 +89,22 @@ struct GatherArgs {
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
 
 // ---- gemm.hip
+// NVFP4 output of the GEMM's fused encode: Y [M, N] with 1-D blocks.
+struct QuantOut {
+    uint8_t *codes;         // [M, N / 2]
+    uint8_t *scales;        // [M, N / 16]
+    float *s_dec;           // one float
+    const float *amax_in;   // tensor amax the encode uses (device)
+    int four_over_six;
+};
+// quant == nullptr: Y in ydtype at y.  Otherwise Y goes to *quant (y and
+// ydtype unused, no LoRA).
 hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_sdec,
                             const uint8_t *w_codes, const uint8_t *w_scales,
                             const float *w_sdec, int64_t M, int64_t N, int64_t K, int w_layout,
                             void *y, int ydtype, float *amax_out, const uint16_t *lora_xa,
                             const uint16_t *lora_b, int64_t lora_r, float lora_scale,
-                            hipStream_t s);
+                            const QuantOut *quant, hipStream_t s);
 hipError_t launch_lora_down(const uint16_t *x, const uint16_t *a, int64_t M, int64_t K, int64_t r,
                             uint16_t *xa, hipStream_t s);
 hipError_t launch_gemm_mx(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *w_codes,

@@ -88,6 +88,26 @@ def test_dequantize_and_gemm_validation(L):
     assert L.nvfp4_gemm_w4a4(C.byref(a), C.byref(w), FAKE, 1, FAKE + 2, None) == -2  # amax_out
 
 
+def test_gemm_quant_validation(L):
+    # nvfp4_gemm_w4a4_quant(a, w, y, search, amax_in, amax_out, stream)
+    a, w = tensor(64, 64), tensor(32, 64, nv.LAYOUT_2D)
+    y = tensor(64, 32)
+    g = lambda yt, **kw: L.nvfp4_gemm_w4a4_quant(
+        C.byref(kw.get("a", a)), C.byref(w), C.byref(yt) if yt else None, kw.get("search", 1),
+        kw.get("amax_in", FAKE), kw.get("amax_out", None), None)
+    assert g(None) == -1                                  # NULL y
+    assert g(tensor(64, 32, nv.LAYOUT_2D)) == -1          # Y must be 1-D
+    assert g(tensor(48, 32)) == -3                        # rows != M
+    assert g(tensor(64, 48)) == -3                        # cols != N
+    assert g(y, search=2) == -1
+    assert g(y, amax_in=None) == -1
+    assert b"amax_in" in L.nvfp4_last_error()
+    assert g(y, amax_in=FAKE + 2) == -2
+    assert g(y, amax_out=FAKE + 1) == -2
+    assert g(y, a=tensor(64, 64, nv.LAYOUT_2D)) == -1     # A must be 1-D
+    assert g(tensor(64, 32, codes=FAKE + 8)) == -2
+
+
 def test_quantize_rht_validation(L):
     # nvfp4_quantize_rht(x, dtype, out, search, signs, amax_in, ws, ws_bytes, stream)
     t1, t2 = tensor(32, 64), tensor(32, 64, nv.LAYOUT_2D)
