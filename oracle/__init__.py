@@ -90,6 +90,9 @@ def _declare(L):
     L.orc_lora_ref.argtypes = [_f32p, _f32p, _f32p, _i64, _i64, _i64, _i64, C.c_float,
                                C.c_void_p, _i64, _f64p, C.c_void_p, C.c_void_p]
     L.orc_lora_ref.restype = C.c_int
+    L.orc_attention_ref.argtypes = [_f32p, _f32p, _f32p, _i64, _i64, _i64, _i64, C.c_double,
+                                    C.c_void_p, _i64, _f64p, C.c_void_p, C.c_void_p]
+    L.orc_attention_ref.restype = C.c_int
 
 
 def _f32(a):
@@ -332,3 +335,32 @@ def lora_ref(x, a, b, scale: float, rows=None):
     if rc != 0:
         raise RuntimeError("orc_lora_ref failed")
     return y, s, xa
+
+
+# --------------------------------------------------------------------------
+# Attention over the effective set
+# --------------------------------------------------------------------------
+
+def attention_ref(q, k, v, scale: float, rows=None):
+    """Softmax attention per head in double: q [nq, H, d], k and v [nk, H, d]
+    float32 (bf16 values).  Returns (o fp64 [len(rows) or nq, H, d],
+    sum_j w_j |v_j| / sum_j w_j of the same shape, lse fp64 [.., H])."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    nq, H, d = q.shape
+    nk = k.shape[0]
+    if k.shape != (nk, H, d) or v.shape != (nk, H, d):
+        raise ValueError("attention_ref: k and v must be [nk, H, d] like q")
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, np.int64)
+    nr = len(rows) if rows is not None else nq
+    o = np.empty((nr, H, d), np.float64)
+    ao = np.empty((nr, H, d), np.float64)
+    lse = np.empty((nr, H), np.float64)
+    kk = k.reshape(-1) if k.size else np.zeros(1, np.float32)
+    vv = v.reshape(-1) if v.size else np.zeros(1, np.float32)
+    rc = lib().orc_attention_ref(q.reshape(-1), kk, vv, nq, nk, H, d, float(scale),
+                                 rows.ctypes.data if rows is not None else None, nr,
+                                 o.reshape(-1), ao.ctypes.data, lse.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("orc_attention_ref failed")
+    return o, ao, lse

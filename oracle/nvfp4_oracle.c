@@ -572,3 +572,86 @@ int orc_lora_ref(const float *x, const float *a, const float *b, int64_t M, int6
     free(xr);
     return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* Attention over the effective key/value set                         */
+/* ------------------------------------------------------------------ */
+
+/* [DR] Multi-Shot Attention Sink: each step's sliding-window
+ * self-attention runs over the effective set K_eff(t) = A_g u A_s u
+ * KV[t-W, t) of dequantized keys and values.  READING: scaled dot-product
+ * softmax attention per head,
+ *   o[i] = sum_j w_j v[j] / sum_j w_j,  w_j = exp(scale q[i].k[j] - m),
+ * m = max_j scale q[i].k[j] (a common factor exp(-m) that cancels), and the
+ * log-sum-exp lse[i] = m + log(sum_j w_j); all in double.  q [nq, H, d],
+ * k and v [nk, H, d] row-major float32 (bf16 values); o [nq, H, d]; abs_o
+ * (optional) receives sum_j w_j |v[j]| / sum_j w_j (the error scale of the
+ * weighted sum); lse [nq, H] (optional).  nk == 0 gives o = 0, lse = -inf.
+ * `rows` (optional) picks the queries computed: output row i is query
+ * rows[i]. */
+int orc_attention_ref(const float *q, const float *k, const float *v, int64_t nq, int64_t nk,
+                      int64_t H, int64_t d, double scale, const int64_t *rows, int64_t nrows,
+                      double *o, double *abs_o, double *lse)
+{
+    int64_t nr = rows ? nrows : nq;
+    double *s = (double *)malloc((size_t)(nk > 0 ? nk : 1) * sizeof(double));
+    double *acc = (double *)malloc((size_t)(2 * d > 0 ? 2 * d : 1) * sizeof(double));
+    if (!s || !acc) {
+        free(s);
+        free(acc);
+        return -2;
+    }
+    double *aacc = acc + d;
+    for (int64_t i = 0; i < nr; ++i) {
+        int64_t qi = rows ? rows[i] : i;
+        if (qi < 0 || qi >= nq) {
+            free(s);
+            free(acc);
+            return -1;
+        }
+        for (int64_t h = 0; h < H; ++h) {
+            const float *qv = q + (qi * H + h) * d;
+            double m = -INFINITY;
+            for (int64_t j = 0; j < nk; ++j) {
+                const float *kv = k + (j * H + h) * d;
+                double dot = 0.0;
+                for (int64_t e = 0; e < d; ++e)
+                    dot += (double)qv[e] * (double)kv[e];
+                s[j] = scale * dot;
+                if (s[j] > m)
+                    m = s[j];
+            }
+            double l = 0.0;
+            for (int64_t j = 0; j < nk; ++j) {
+                s[j] = exp(s[j] - m);
+                l += s[j];
+            }
+            double *out = o + (i * H + h) * d;
+            double *aout = abs_o ? abs_o + (i * H + h) * d : NULL;
+            /* each element's sum runs over j in order; j is the outer loop
+             * only so that the rows of v are read contiguously */
+            for (int64_t e = 0; e < d; ++e) {
+                acc[e] = 0.0;
+                aacc[e] = 0.0;
+            }
+            for (int64_t j = 0; j < nk; ++j) {
+                const float *vr = v + (j * H + h) * d;
+                for (int64_t e = 0; e < d; ++e) {
+                    double x = (double)vr[e];
+                    acc[e] += s[j] * x;
+                    aacc[e] += s[j] * fabs(x);
+                }
+            }
+            for (int64_t e = 0; e < d; ++e) {
+                out[e] = nk > 0 ? acc[e] / l : 0.0;
+                if (aout)
+                    aout[e] = nk > 0 ? aacc[e] / l : 0.0;
+            }
+            if (lse)
+                lse[i * H + h] = nk > 0 ? m + log(l) : -INFINITY;
+        }
+    }
+    free(s);
+    free(acc);
+    return 0;
+}

@@ -47,5 +47,8 @@ int orc_lora_ref(const float *x, const float *a, const float *b, int64_t M, int6
                  int64_t N, int64_t r, float scale, const int64_t *rows, int64_t nrows,
                  double *y, double *abs_sum, float *xa);
 void orc_e4m3_encode_array(const float *t, int64_t n, uint8_t *out);
+int orc_attention_ref(const float *q, const float *k, const float *v, int64_t nq, int64_t nk,
+                      int64_t H, int64_t d, double scale, const int64_t *rows, int64_t nrows,
+                      double *o, double *abs_o, double *lse);
 
 #endif
