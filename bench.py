@@ -18,7 +18,7 @@ recorded around each launch on the launch's own stream, against 8 TB/s.
 bounded sample.  `secondary` carries the W4A4 GEMM (7040x3072x3072, TFLOP/s
 vs the 2.5 PFLOP/s dense fp16/bf16 MFMA peak) and activation quantize lines.
 
-Other workloads (--workload): gemm_attn, ffn, ring64s, quant_act, wgrad, lora.
+Other workloads (--workload): gemm_attn, ffn, ring64s, quant_act, wgrad, lora, attn.
 """
 from __future__ import annotations
 
@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="kv_chunk",
                     choices=["kv_chunk", "gemm_attn", "ffn", "ring64s", "quant_act", "wgrad",
-                             "lora"])
+                             "lora", "attn"])
     ap.add_argument("--sets", type=int, default=4, help="rotated input/output buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
@@ -529,9 +529,18 @@ def attention_context(nv, dev, reps=3):
         return {"gather_us": round(gms * 1e3, 2), "tokens": n, "flash_attention": None,
                 "note": f"flash attention unavailable: {type(e).__name__}"}
     flops = 4.0 * KV_T * n * KV_D * KV_H
+    # the same attention with the dequantization fused in, straight from the ring
+    qt = q[0].permute(1, 0, 2).contiguous()
+    ot = torch.empty_like(qt)
+    fms, _ = time_steps(lambda i: ring.attention(15, qt, out=ot), reps, 1)
+    kt = kernel_times(nv, lambda i: ring.attention(15, qt, out=ot), reps, 0)
     return {"tokens": n, "gather_us": round(gms * 1e3, 2), "flash_attention_ms": round(ams, 3),
             "flash_attention_TFLOP/s": round(flops / ams / 1e9, 1),
-            "gather_share_of_gather_plus_attention": round(gms / (gms + ams), 4)}
+            "gather_share_of_gather_plus_attention": round(gms / (gms + ams), 4),
+            "fused_dequant_attention_ms": round(fms, 3),
+            "fused_dequant_attention_kernel_ms": round(kt["attn_window"][1], 3),
+            "fused_dequant_attention_TFLOP/s": round(flops / fms / 1e9, 1),
+            "fused_vs_gather_plus_flash": round((gms + ams) / fms, 3)}
 
 
 def sustained_sclk_mhz(nv, dev, seconds=0.6):
@@ -595,7 +604,9 @@ def main():
 
     if args.workload != "kv_chunk":
         fn = {"gemm_attn": run_gemm_attn, "ffn": run_ffn, "ring64s": run_ring64s,
-              "quant_act": run_quant_act, "wgrad": run_wgrad, "lora": run_lora}[args.workload]
+              "quant_act": run_quant_act, "wgrad": run_wgrad, "lora": run_lora,
+              "attn": lambda nv, args, dev: attention_context(nv, dev, max(3, args.steps // 10))
+              }[args.workload]
         r = fn(nv, args, dev)
         for key in ("kernels", "fused_kernels"):
             if key in r:

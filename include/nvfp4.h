@@ -343,6 +343,30 @@ int nvfp4_kv_effective_tokens(const nvfp4_kv_ring *ring, int64_t step, int64_t *
 int nvfp4_gather_window(const nvfp4_kv_ring *ring, int64_t step, void *K_out, void *V_out,
                         int64_t capacity_tokens, int64_t *n_tokens, void *stream);
 
+/*
+ * Attention of step `step`'s queries over K_eff(step), read packed from the
+ * ring with the dequantization fused in (DeepRead summary, Multi-Shot
+ * Attention Sink: sliding-window self-attention over K_eff(t) = A_g u A_s u
+ * KV[t-W, t); TX page, NVFP4 section: the FP4 KV cache with a fused
+ * dequantization extension).  Per head hh and query i:
+ *   o[i, hh] = sum_j softmax_j(softmax_scale * q[i, hh] . K_hat[j, hh]) V_hat[j, hh]
+ *   lse[i, hh] = ln sum_j exp(softmax_scale * q[i, hh] . K_hat[j, hh])
+ * over the tokens j of K_eff(step), with K_hat and V_hat the bf16 values
+ * nvfp4_gather_window would write (so the result equals attention over the
+ * gathered K/V).  Scores and sums in fp32 (the products on the bf16 MFMA),
+ * the softmax weights rounded to bf16 for the value product, o rounded to
+ * bf16 (nearest-even).
+ *   step: must equal ring->next_chunk, as for the gather.
+ *   q, o: device bf16 [n_q, H, 128], row-major, 16-byte aligned; head_dim
+ *     must be 128 (else NVFP4_ESHAPE).
+ *   lse: NULL, or device fp32 [n_q, H] (for merging with attention over
+ *     other keys, e.g. the chunk's own).
+ *   An empty K_eff (step 0) gives o = 0 and lse = -inf.  One kernel launch.
+ */
+int nvfp4_attention_window(const nvfp4_kv_ring *ring, int64_t step, const void *q_bf16,
+                           int64_t n_q, float softmax_scale, void *o_bf16, float *lse,
+                           void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* Kernel timing                                                              */
 /* ------------------------------------------------------------------------ */

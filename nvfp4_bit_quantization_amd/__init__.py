@@ -96,6 +96,8 @@ _EXPORTS = {
                                   C.c_int),
     "nvfp4_gather_window": ([C.POINTER(CKvRing), C.c_int64, C.c_void_p, C.c_void_p, C.c_int64,
                              C.POINTER(C.c_int64), C.c_void_p], C.c_int),
+    "nvfp4_attention_window": ([C.POINTER(CKvRing), C.c_int64, C.c_void_p, C.c_int64, C.c_float,
+                                C.c_void_p, C.c_void_p, C.c_void_p], C.c_int),
     "nvfp4_profile_enable": ([C.c_int], C.c_int),
     "nvfp4_profile_collect": ([C.c_char_p, C.c_int, C.c_void_p, C.c_void_p, C.c_int], C.c_int),
 }
@@ -442,6 +444,27 @@ class KVRing:
                                          _dev(V_out, "V_out"), cap, C.byref(got),
                                          _stream(stream)))
         return K_out[:got.value], V_out[:got.value]
+
+    def attention(self, step: int, q: torch.Tensor, softmax_scale: float | None = None,
+                  out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                  stream=None) -> torch.Tensor:
+        """nvfp4_attention_window: attention of q (bf16 [n_q, heads, 128]) over
+        K_eff(step), read packed from the ring.  softmax_scale defaults to
+        1/sqrt(head_dim); lse (optional float32 [n_q, heads]) receives the
+        log-sum-exp of the scaled scores."""
+        if q.dtype != torch.bfloat16 or q.dim() != 3 or q.shape[1:] != (self.cfg.heads,
+                                                                        self.cfg.head_dim):
+            raise ValueError(f"q must be bfloat16 [n_q, {self.cfg.heads}, {self.cfg.head_dim}]")
+        if softmax_scale is None:
+            softmax_scale = self.cfg.head_dim ** -0.5
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is not None and (lse.dtype != torch.float32 or lse.shape != q.shape[:2]):
+            raise ValueError("lse must be float32 [n_q, heads]")
+        _check(lib().nvfp4_attention_window(
+            C.byref(self.ring), step, _dev(q, "q"), q.shape[0], float(softmax_scale),
+            _dev(out, "out"), None if lse is None else _dev(lse, "lse"), _stream(stream)))
+        return out
 
 
 # --------------------------------------------------------------------------

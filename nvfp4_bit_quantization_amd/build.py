@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libnvfp4.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["quantize.hip", "kv.hip", "gemm.hip", "capi.cpp", "profile.cpp"]
+SOURCES = ["quantize.hip", "kv.hip", "gemm.hip", "attn.hip", "capi.cpp", "profile.cpp"]
 HEADERS = ["device.hpp", "launch.hpp"]
 
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")

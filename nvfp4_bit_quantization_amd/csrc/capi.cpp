@@ -538,4 +538,68 @@ int nvfp4_gather_window(const nvfp4_kv_ring *ring, int64_t step, void *K_out, vo
     return hip_status(e, "gather_window launch");
 }
 
+int nvfp4_attention_window(const nvfp4_kv_ring *ring, int64_t step, const void *q_bf16,
+                           int64_t n_q, float softmax_scale, void *o_bf16, float *lse,
+                           void *stream) {
+    int st = check_ring(ring);
+    if (st) return st;
+    if (step != ring->next_chunk)
+        return fail(NVFP4_ESTATE, "attention_window: step %lld != next chunk %lld",
+                    (long long)step, (long long)ring->next_chunk);
+    if (ring->cfg.head_dim != 128)
+        return fail(NVFP4_ESHAPE, "attention_window: head_dim must be 128 (got %d)",
+                    ring->cfg.head_dim);
+    if (n_q < 0) return fail(NVFP4_ESHAPE, "attention_window: negative query count");
+    if (!(softmax_scale == softmax_scale) || softmax_scale > 3.0e38f || softmax_scale < -3.0e38f)
+        return fail(NVFP4_EINVAL, "attention_window: softmax_scale must be finite");
+    if (n_q > 0 && (!q_bf16 || !o_bf16))
+        return fail(NVFP4_EINVAL, "attention_window: NULL q or o");
+    if (!aligned16(q_bf16) || !aligned16(o_bf16) || ((uintptr_t)lse & 3u))
+        return fail(NVFP4_EALIGN, "attention_window: q and o must be 16-byte aligned, lse 4");
+    if ((n_q + 255) / 256 * (int64_t)ring->cfg.heads >= ((int64_t)1 << 31))
+        return fail(NVFP4_ESHAPE, "attention_window: too many queries");
+    const Plan p = plan_effective(ring, step);
+    const nvfp4_kv_config &c = ring->cfg;
+    const int64_t T = ring->chunk_tokens, hd = ring->hd;
+    nvfp4::AttnArgs a{};
+    int ns = 0;
+    auto add = [&](const nvfp4::KvRegion &r, int64_t skip, int64_t n) {
+        nvfp4::AttnSeg &s = a.seg[ns++];
+        s.kc = r.kc + skip * hd / 2;
+        s.ks = r.ks + skip * hd / 16;
+        s.vc = r.vc + skip * hd / 2;
+        s.vs = r.vs + skip * hd / 16;
+        s.mu = r.mu;
+        s.sd = r.sd;
+        s.n = n;
+    };
+    // the same segments as the gather, in ascending token order
+    if (p.n_g > 0)
+        add(region_at(ring->base + ring->gsink_offset,
+                      region_layout((int64_t)c.sink_frames_global * c.tokens_per_frame, hd)),
+            0, p.n_g);
+    if (p.n_s > 0) {
+        const int64_t skip = (ring->s_start > p.n_g ? ring->s_start : p.n_g) - ring->s_start;
+        add(region_at(ring->base + ring->ssink_offset,
+                      region_layout((int64_t)c.sink_frames_shot * c.tokens_per_frame, hd)),
+            skip, p.n_s);
+    }
+    for (int64_t w = 0; w < p.nwin; ++w)
+        add(region_at(ring->base + ((p.c_lo + w) % c.window_chunks) * ring->slot_bytes,
+                      region_layout(T, hd)),
+            0, T);
+    a.nseg = ns;
+    a.tile0[0] = 0;
+    for (int i = 0; i < ns; ++i) a.tile0[i + 1] = a.tile0[i] + (int32_t)((a.seg[i].n + 63) / 64);
+    a.heads = c.heads;
+    a.HD = hd;
+    a.nq = n_q;
+    a.q = (const uint16_t *)q_bf16;
+    a.o = (uint16_t *)o_bf16;
+    a.lse = lse;
+    a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    hipError_t e = nvfp4::launch_attn_window(a, (hipStream_t)stream);
+    return hip_status(e, "attention_window launch");
+}
+
 }  // extern "C"

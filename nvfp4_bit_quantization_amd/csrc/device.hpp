@@ -24,6 +24,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef double f64x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -210,13 +211,13 @@ __device__ __forceinline__ float wave_max(float v) {
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Two floats to packed bf16 (nearest-even), a in the low half.
+// Two floats to packed bf16 (nearest-even), a in the low half: one
+// v_cvt_pk_bf16_f32 with both sources.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    __bf16 ha = (__bf16)a, hb = (__bf16)b;
-    unsigned short ua, ub;
-    __builtin_memcpy(&ua, &ha, 2);
-    __builtin_memcpy(&ub, &hb, 2);
-    return (uint32_t)ua | ((uint32_t)ub << 16);
+    const bf16x2 v = __builtin_convertvector(f32x2{a, b}, bf16x2);
+    uint32_t u;
+    __builtin_memcpy(&u, &v, 4);
+    return u;
 }
 
 // Raw 16-element block loads (16 bf16 = 2 x 16 B, 16 float = 4 x 16 B).

@@ -523,7 +523,7 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
 // Raise the dynamic-LDS limit of `fns` to `bytes` once per device: `done`
 // holds one bit per device id (0..31) already set up.  Threads that race
 // both set the attribute, which is harmless.
-static hipError_t lds_limit_once(const void *const *fns, int n, int bytes,
+hipError_t lds_limit_once(const void *const *fns, int n, int bytes,
                                  std::atomic<uint32_t> &done) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace nvfp4 {
 
 // ---- profile.cpp: optional HIP-event timing of every launch
@@ -88,7 +90,36 @@ struct GatherArgs {
 };
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
 
+// ---- attn.hip
+// Attention over K_eff(t) read packed from the ring: the effective set as
+// up to 2 + W segments, each a run of consecutive tokens of one region (one
+// key mean, one pair of decode scales), in ascending token order.
+constexpr int kAttnMaxSeg = 2 + 16;
+struct AttnSeg {
+    const uint8_t *kc, *ks, *vc, *vs;  // codes / scales of the segment's first token
+    const float *mu;                   // [HD] key mean of the region
+    const float *sd;                   // [2] decode scales (K_s, V)
+    int64_t n;                         // tokens
+};
+struct AttnArgs {
+    AttnSeg seg[kAttnMaxSeg];
+    int32_t tile0[kAttnMaxSeg + 1];  // first 64-key tile of each segment, tile0[nseg] = total
+    int32_t nseg;
+    int32_t heads;
+    int64_t HD;                      // heads * 128
+    int64_t nq;
+    const uint16_t *q;               // [nq, heads, 128] bf16
+    uint16_t *o;                     // [nq, heads, 128] bf16
+    float *lse;                      // [nq, heads] or nullptr
+    float scale_log2;                // softmax scale * log2(e)
+};
+hipError_t launch_attn_window(const AttnArgs &a, hipStream_t s);
+
 // ---- gemm.hip
+// Raise the dynamic-LDS limit of the kernels `fns` to `bytes`, once per
+// device (`done`: one bit per device id).
+hipError_t lds_limit_once(const void *const *fns, int n, int bytes, std::atomic<uint32_t> &done);
+
 // NVFP4 output of the GEMM's fused encode: Y [M, N] with 1-D blocks.
 struct QuantOut {
     uint8_t *codes;         // [M, N / 2]

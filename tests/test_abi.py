@@ -184,6 +184,29 @@ def test_ring_validation(L):
     assert n.value == 2 * 7040
 
 
+def test_attention_window_validation(L):
+    # nvfp4_attention_window(ring, step, q, n_q, scale, o, lse, stream): every
+    # call below is rejected on the host before a launch
+    r = make_ring(L)
+    a = lambda **kw: L.nvfp4_attention_window(
+        C.byref(kw.get("ring", r)), kw.get("step", 0), kw.get("q", FAKE), kw.get("nq", 64),
+        kw.get("scale", 0.088), kw.get("o", FAKE), kw.get("lse", None), None)
+    assert a(step=1) == -5                         # not the next chunk
+    assert a(nq=-1) == -3
+    assert a(scale=float("nan")) == -1
+    assert a(scale=float("inf")) == -1
+    assert a(q=None) == -1
+    assert a(o=None) == -1
+    assert a(q=FAKE + 2) == -2
+    assert a(lse=FAKE + 1) == -2
+    c64 = nv.KVConfig(head_dim=64).c()
+    r64 = nv.CKvRing()
+    assert L.nvfp4_kv_ring_init(C.byref(r64), C.byref(c64), FAKE,
+                                L.nvfp4_kv_ring_bytes(C.byref(c64))) == 0
+    assert a(ring=r64) == -3                       # head_dim must be 128
+    assert b"128" in L.nvfp4_last_error()
+
+
 def test_ring_plan_matches_oracle(L, orc):
     """The host planner's |K_eff(t)| equals the oracle's brute force, for
     several geometries and shot schedules (white-box: the ring's counters are

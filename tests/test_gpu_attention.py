@@ -1,0 +1,173 @@
+"""GPU parity: attention over K_eff(t) read packed from the ring (the
+dequantization fused in), against the oracle's double-precision attention
+over the oracle's own gather of the same chunks.
+
+Bar, per output element (q, head, e):
+  |o - o_ref| <= 2^-8 (A + |o_ref|) + 2^-16 scale |q| max_j |k_j| A
+with A = sum_j w_j |v_j| / sum_j w_j (the oracle's abs-weighted value).  The
+GPU rounds the softmax weights to bf16 for the value product while its
+normaliser sums them unrounded (at most 2^-9 A), rounds o to bf16 (2^-9 |o|),
+and forms the scores in fp32 from exact bf16 products: a 128-term fp32 sum
+is off by at most 128 * 2^-24 sum_e |q_e k_e| <= 2^-17 |q| |k_j|, which moves
+each weight by at most that much relative (x2 for the normaliser); the fp32
+sums over the tiles add ~2^-15 relative at the sizes here.  The bound takes
+twice the two bf16 terms.  lse: |lse - lse_ref| <= 2^-16 scale |q| max|k| +
+2^-14 (1 + |lse_ref|).
+"""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import nvfp4_bit_quantization_amd as m
+
+    m.lib()
+    return m
+
+
+def bf16_gpu(bits, shape):
+    return torch.from_numpy(bits.view(np.int16).reshape(shape)).view(torch.bfloat16).cuda()
+
+
+def f32_of_bits(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def queries(seed, n, H, d):
+    _, qb = synth.kv_chunk(seed, 0, n, H, d)  # N(0, 1) values rounded to bf16
+    return qb.reshape(n, H, d), f32_of_bits(qb).reshape(n, H, d)
+
+
+def check(nv, orc, ring, chunks, cfg, t, shot, qbits, qf, rows=None):
+    Tc, H, d = cfg.chunk_tokens, cfg.heads, cfg.head_dim
+    g_tok = cfg.sink_frames_global * cfg.tokens_per_frame
+    s_tok = cfg.sink_frames_shot * cfg.tokens_per_frame
+    scale = d ** -0.5
+    nq = qf.shape[0]
+    lse = torch.empty((nq, H), dtype=torch.float32, device="cuda")
+    o = ring.attention(t, bf16_gpu(qbits, (nq, H, d)), scale, lse=lse)
+    _, Kr, Vr = orc.gather_window(chunks, t, Tc, cfg.window_chunks, g_tok, shot * Tc, s_tok)
+    k = f32_of_bits(Kr).reshape(-1, H, d)
+    v = f32_of_bits(Vr).reshape(-1, H, d)
+    o_ref, a_ref, lse_ref = orc.attention_ref(qf, k, v, scale, rows=rows)
+    torch.cuda.synchronize()
+    sel = slice(None) if rows is None else torch.from_numpy(np.asarray(rows)).cuda()
+    og = o[sel].float().cpu().numpy().astype(np.float64)
+    lg = lse[sel].cpu().numpy().astype(np.float64)
+    if k.shape[0] == 0:
+        assert np.all(og == 0) and np.all(np.isneginf(lg)), f"step {t}: empty set"
+        return
+    qsel = qf if rows is None else qf[rows]
+    qn = np.linalg.norm(qsel.astype(np.float64), axis=2)                  # [n, H]
+    kmax = np.linalg.norm(k.astype(np.float64), axis=2).max(axis=0)        # [H]
+    sc = 2.0 ** -16 * scale * qn * kmax[None, :]
+    tol = 2.0 ** -8 * (a_ref + np.abs(o_ref)) + sc[..., None] * a_ref
+    err = np.abs(og - o_ref)
+    worst = np.unravel_index(np.argmax(err - tol), err.shape)
+    assert np.all(err <= tol), f"step {t}: o off at {worst}: {err[worst]} > {tol[worst]}"
+    ltol = sc + 2.0 ** -14 * (1 + np.abs(lse_ref))
+    assert np.all(np.abs(lg - lse_ref) <= ltol), f"step {t}: lse off"
+
+
+def small_cfg(nv, **kw):
+    base = dict(tokens_per_frame=16, frames_per_chunk=4, heads=2, head_dim=128,
+                sink_frames_global=1, sink_frames_shot=2, window_chunks=2)
+    base.update(kw)
+    return nv.KVConfig(**base)
+
+
+def drive(nv, orc, cfg, cuts, steps, seed, at_step):
+    ring = nv.KVRing(cfg)
+    Tc, H, d = cfg.chunk_tokens, cfg.heads, cfg.head_dim
+    chunks, shot = {}, 0
+    for t in range(steps):
+        if t in cuts:
+            shot = t
+            ring.begin_shot(t)
+        at_step(ring, chunks, t, shot)
+        kb, vb = synth.kv_chunk(seed, t, Tc, H, d)
+        ring.store_chunk(t, bf16_gpu(kb, (Tc, H, d)), bf16_gpu(vb, (Tc, H, d)))
+        chunks[t] = orc.kv_encode_chunk(f32_of_bits(kb).reshape(Tc, H * d),
+                                        f32_of_bits(vb).reshape(Tc, H * d), search=cfg.search)
+
+
+def test_attention_every_step_small_ring(nv, orc):
+    """Tc = 64, 2 heads, W = 2, a 16-token global sink and a 32-token shot
+    sink, shot cuts at 0 and 4: empty set, sink-only, partial 64-key tiles,
+    up to four segments; 100 queries (a ragged query tile)."""
+    cfg = small_cfg(nv)
+    qbits, qf = queries(3001, 100, cfg.heads, cfg.head_dim)
+
+    def at(ring, chunks, t, shot):
+        print("case: attention small ring step", t, flush=True)
+        check(nv, orc, ring, chunks, cfg, t, shot, qbits, qf)
+
+    drive(nv, orc, cfg, {0, 4}, 8, 3002, at)
+
+
+@pytest.mark.parametrize("nq", [1, 129, 300])
+def test_attention_query_counts(nv, orc, nq):
+    cfg = small_cfg(nv, tokens_per_frame=40, window_chunks=3)  # Tc = 160: 2.5 tiles a chunk
+    qbits, qf = queries(3003 + nq, nq, cfg.heads, cfg.head_dim)
+
+    def at(ring, chunks, t, shot):
+        if t == 5:
+            print("case: attention nq", nq, flush=True)
+            check(nv, orc, ring, chunks, cfg, t, shot, qbits, qf)
+
+    drive(nv, orc, cfg, {0, 3}, 6, 3004, at)
+
+
+def test_attention_64s_ring_step_15_sampled(nv, orc):
+    """The 64 s ring (7040 tokens x 24 heads x 128 a chunk, W = 4, 3-frame
+    sinks, shots at 0 and 10) at step 15: 7040 queries over the 33,440-token
+    set (2640 + 2640 sink tokens and 4 window chunks), the launch the bench
+    times; 12 sampled queries (first and last included) x 24 heads against
+    the oracle."""
+    print("case: attention 64 s ring step 15", flush=True)
+    cfg = nv.KVConfig()
+    Tc, H, d = cfg.chunk_tokens, cfg.heads, cfg.head_dim
+    # chunks 1..9 leave the set before step 15: they reuse chunk 0's values
+    need = [0, 10, 11, 12, 13, 14]
+
+    def make(t):
+        kb, vb = synth.kv_chunk(3005, t, Tc, H, d)
+        enc = orc.kv_encode_chunk(f32_of_bits(kb).reshape(Tc, H * d),
+                                  f32_of_bits(vb).reshape(Tc, H * d))
+        return kb, vb, enc
+
+    with ThreadPoolExecutor(max_workers=6) as ex:
+        made = dict(zip(need, ex.map(make, need)))
+    chunks = {t: made[t][2] for t in need}
+    ring = nv.KVRing(cfg)
+    for t in range(15):
+        if t % 10 == 0:
+            ring.begin_shot(t)
+        kb, vb, _ = made.get(t, made[0])
+        ring.store_chunk(t, bf16_gpu(kb, (Tc, H, d)), bf16_gpu(vb, (Tc, H, d)))
+    assert ring.effective_tokens(15) == 33440
+    qbits, qf = queries(3006, Tc, H, d)
+    rows = np.unique(np.concatenate([[0, 127, 128, Tc - 1],
+                                     np.random.default_rng(7).integers(0, Tc, 8)]))
+    check(nv, orc, ring, chunks, cfg, 15, 10, qbits, qf, rows=rows)
+
+
+def test_attention_validation(nv):
+    cfg = small_cfg(nv)
+    ring = nv.KVRing(cfg)
+    q = torch.zeros((4, 2, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(RuntimeError):
+        ring.attention(1, q)  # step != next chunk
+    with pytest.raises(ValueError):
+        ring.attention(0, q[:, :1])  # wrong head count
+    ring64 = nv.KVRing(small_cfg(nv, head_dim=64))
+    with pytest.raises(RuntimeError):
+        ring64.attention(0, torch.zeros((4, 2, 64), dtype=torch.bfloat16, device="cuda"))
