@@ -19,8 +19,8 @@
 // MFMAs).  The effective set is walked segment by segment (each segment one
 // region: one key mean, one pair of decode scales), 64 keys a tile, through
 // two LDS stages.  Every tile is dequantized once per workgroup straight
-// from the packed ring (waves 0-3 the V blocks, 2 keys x 16 d a lane; waves
-// 4-7 the K blocks, 2 keys x 16 d a lane) into
+// from the packed ring (every lane one K block and half a V block for a
+// pair of keys) into
 //   K tile   [64 keys][128 d] bf16: 16-byte column c of key k in slot c ^ (k & 15)
 //   V^T tile [128 d][64 keys] bf16: keys permuted (below); 16-byte slot s of
 //            row d in s ^ ((d >> 1) & 7) ^ ((d >> 4) & 7)
@@ -34,9 +34,9 @@
 // each 16-key group at column ((k >> 2) & 1) * 8 + ((k >> 3) & 1) * 4 + (k & 3),
 // so the 8 keys of a lane's P^T operand slots are 16 contiguous bytes of V^T.
 // Each wave's queries sit in LDS too (same swizzle as the K tile), read one
-// 16-deep fragment at a time.  The global loads of tile j + 1 are issued
-// before tile j's MFMAs and dequantized into the other stage after them; one
-// barrier per tile.
+// 16-deep fragment at a time.  The packed blocks of tile j + 2 are loaded
+// during tile j, and tile j + 1 is dequantized into the other stage in the
+// same instruction stream as tile j's value MFMAs; one barrier per tile.
 #include <atomic>
 
 #include "device.hpp"
@@ -66,86 +66,101 @@ __device__ __forceinline__ int seg_of(const AttnArgs &a, int j) {
     return s;
 }
 
-// One lane's packed blocks of a tile: 2 keys x one 16-element block along d.
-// A key past the segment's end reads the segment's last token instead: its
-// score is masked to -inf, so its weight is exactly 0 and its (finite)
-// values never count.
+// One lane's packed blocks of a tile: one K block (16 d of one key) and, of
+// V, the 8 d of one half block for a pair of keys.  A key past the
+// segment's end reads the segment's last token instead: its score is masked
+// to -inf, so its weight is exactly 0 and its (finite) values never count.
 struct TileBlocks {
-    u32x2 c[2];
-    uint32_t sc[2];
+    u32x2 kc;
+    uint32_t ks;
+    uint32_t vc[2];
+    uint32_t vs[2];
 };
 
-// V lanes (waves 0-3, t = threadIdx.x): keys 2 (t >> 3) + i, d block t & 7.
-// K lanes (waves 4-7, t = threadIdx.x - 256): keys (t >> 3) + 32 i, d block t & 7.
-__device__ __forceinline__ int tile_key(bool vrole, int t, int i) {
-    return vrole ? 2 * (t >> 3) + i : (t >> 3) + 32 * i;
+// Lane t (0..511) of the workgroup: K block of key t >> 3, d block t & 7;
+// V keys 2 (t >> 4) and 2 (t >> 4) + 1, d = 8 (t & 15) .. + 8.  Raw buffer
+// loads over the segment's arrays: the head's offset is the scalar part,
+// token * row bytes (below 2^31, tokens below 2^24) the 24-bit vector part.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t seg_rsrc(const void *p, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
+                                             kBufferWord3);
 }
 
-__device__ __forceinline__ void load_blocks(const AttnArgs &a, const AttnSeg &sg, int64_t tok0,
-                                            bool vrole, int t, int head, TileBlocks &tb) {
-    const int b = t & 7;
-    const uint8_t *codes = vrole ? sg.vc : sg.kc;
-    const uint8_t *scales = vrole ? sg.vs : sg.ks;
-    const int64_t cstride = a.HD >> 1, sstride = a.HD >> 4;
+__device__ __forceinline__ void load_blocks(const AttnArgs &a, const AttnSeg &sg, int tok0, int t,
+                                            int head, TileBlocks &tb) {
+    const uint32_t cs = (uint32_t)(a.HD >> 1), ss = (uint32_t)(a.HD >> 4);
+    const int last = (int)sg.n - 1;
+    const __amdgpu_buffer_rsrc_t kc = seg_rsrc(sg.kc, sg.n * cs), ks = seg_rsrc(sg.ks, sg.n * ss);
+    const __amdgpu_buffer_rsrc_t vc = seg_rsrc(sg.vc, sg.n * cs), vs = seg_rsrc(sg.vs, sg.n * ss);
+    {
+        const int tk = tok0 + (t >> 3) < last ? tok0 + (t >> 3) : last;
+        const int b = t & 7;
+        tb.kc = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                              kc, __umul24(tk, cs) + b * 8, head * 64, 0));
+        tb.ks = __builtin_amdgcn_raw_buffer_load_b8(ks, __umul24(tk, ss) + b, head * 8, 0);
+    }
+    const int hb = t & 15;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        int64_t tok = tok0 + tile_key(vrole, t, i);
-        tok = tok < sg.n ? tok : sg.n - 1;
-        tb.c[i] = *(const u32x2 *)(codes + tok * cstride + head * 64 + b * 8);
-        tb.sc[i] = scales[tok * sstride + head * 8 + b];
+        const int tv = tok0 + 2 * (t >> 4) + i < last ? tok0 + 2 * (t >> 4) + i : last;
+        tb.vc[i] = __builtin_amdgcn_raw_buffer_load_b32(vc, __umul24(tv, cs) + hb * 4, head * 64, 0);
+        tb.vs[i] = __builtin_amdgcn_raw_buffer_load_b8(vs, __umul24(tv, ss) + (hb >> 1), head * 8, 0);
     }
 }
 
-// Dequantize a lane's blocks into `stage` (K rows or V^T columns).
-__device__ __forceinline__ void store_blocks(uint8_t *stage, const AttnSeg &sg, bool vrole, int t,
-                                             int head, const TileBlocks &tb) {
-    const int b = t & 7;
-    if (vrole) {
-        const float sdv = sg.sd[1];
-        float S[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) S[i] = e4m3_value(tb.sc[i]) * sdv;
-        const int col = vt_col(2 * (t >> 3));  // 2 consecutive columns
-        const int slot = col >> 3, off = (col & 7) * 2;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            float y[2][8];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) dequant8(half ? tb.c[i].y : tb.c[i].x, S[i], y[i]);
-#pragma unroll
-            for (int dd = 0; dd < 8; ++dd) {
-                const int d = b * 16 + half * 8 + dd;
-                const int phys = slot ^ ((d >> 1) & 7) ^ ((d >> 4) & 7);
-                *(uint32_t *)(stage + kATile + d * 128 + phys * 16 + off) =
-                    pack_bf16x2(y[0][dd], y[1][dd]);
-            }
-        }
-    } else {
-        const float sdk = sg.sd[0];
+// Dequantize a lane's blocks into `stage`: a K row segment and V^T columns.
+__device__ __forceinline__ void store_blocks(uint8_t *stage, const AttnSeg &sg, int t, int head,
+                                             const TileBlocks &tb) {
+    {
+        const int k = t >> 3, b = t & 7;
         Raw16F32 m;
-        load_raw16(sg.mu + head * kAD + b * 16, m);
+        buffer_load16(seg_rsrc(sg.mu, (int64_t)head * kAD * 4 + kAD * 4), (uint32_t)(head * kAD + b * 16) * 4, m);
         float mu[16];
         unpack16(m, mu);
+        const float S = e4m3_value(tb.ks) * sg.sd[0];
+        float y0[8], y1[8];
+        dequant8(tb.kc.x, S, y0);
+        dequant8(tb.kc.y, S, y1);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int k = tile_key(false, t, i);
-            const float S = e4m3_value(tb.sc[i]) * sdk;
-            float y0[8], y1[8];
-            dequant8(tb.c[i].x, S, y0);
-            dequant8(tb.c[i].y, S, y1);
+        for (int e = 0; e < 8; ++e) {
+            y0[e] = y0[e] + mu[e];
+            y1[e] = y1[e] + mu[8 + e];
+        }
+        const u32x4 lo{pack_bf16x2(y0[0], y0[1]), pack_bf16x2(y0[2], y0[3]),
+                       pack_bf16x2(y0[4], y0[5]), pack_bf16x2(y0[6], y0[7])};
+        const u32x4 hi{pack_bf16x2(y1[0], y1[1]), pack_bf16x2(y1[2], y1[3]),
+                       pack_bf16x2(y1[4], y1[5]), pack_bf16x2(y1[6], y1[7])};
+        *(u32x4 *)(stage + k * 256 + (((2 * b) ^ (k & 15)) * 16)) = lo;
+        *(u32x4 *)(stage + k * 256 + (((2 * b + 1) ^ (k & 15)) * 16)) = hi;
+    }
+    {
+        const float sdv = sg.sd[1];
+        float y[2][8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                y0[e] = y0[e] + mu[e];
-                y1[e] = y1[e] + mu[8 + e];
-            }
-            const u32x4 lo{pack_bf16x2(y0[0], y0[1]), pack_bf16x2(y0[2], y0[3]),
-                           pack_bf16x2(y0[4], y0[5]), pack_bf16x2(y0[6], y0[7])};
-            const u32x4 hi{pack_bf16x2(y1[0], y1[1]), pack_bf16x2(y1[2], y1[3]),
-                           pack_bf16x2(y1[4], y1[5]), pack_bf16x2(y1[6], y1[7])};
-            *(u32x4 *)(stage + k * 256 + (((2 * b) ^ (k & 15)) * 16)) = lo;
-            *(u32x4 *)(stage + k * 256 + (((2 * b + 1) ^ (k & 15)) * 16)) = hi;
+        for (int i = 0; i < 2; ++i) dequant8(tb.vc[i], e4m3_value(tb.vs[i]) * sdv, y[i]);
+        const int col = vt_col(2 * (t >> 4));  // two consecutive columns
+        const int slot = col >> 3, off = (col & 7) * 2;
+        const int hb = t & 15;
+#pragma unroll
+        for (int dd = 0; dd < 8; ++dd) {
+            const int d = hb * 8 + dd;
+            const int phys = slot ^ ((d >> 1) & 7) ^ ((d >> 4) & 7);
+            *(uint32_t *)(stage + kATile + d * 128 + phys * 16 + off) = pack_bf16x2(y[0][dd], y[1][dd]);
         }
     }
+}
+
+// max / sum of v over lanes l and l ^ 32 (v_permlane32_swap: the upper half
+// of the first operand trades places with the lower half of the second)
+__device__ __forceinline__ float half_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
@@ -162,8 +177,7 @@ __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = lane & 31, h = lane >> 5;
-    const bool vrole = wave < 4;
-    const int t = vrole ? threadIdx.x : threadIdx.x - 256;
+    const int t = threadIdx.x;
 
     // the wave's queries (Q^T operand rows) into its LDS region: query
     // qw + c in row c, 16-byte column x in slot x ^ (c & 15); lane (c, h)
@@ -186,20 +200,29 @@ __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
         for (int e = 0; e < 16; ++e) o[db][e] = 0.0f;
     float m_run = -__builtin_inff(), l_run = 0.0f;
 
+    // Tile j + 1's blocks (tb, segment s_tb) were loaded one iteration
+    // earlier and are dequantized into the idle stage among tile j's value
+    // MFMAs; tile j + 2's are requested at the top of iteration j.  Past the
+    // last tile the loads repeat it and the extra stage write is never read,
+    // so the loop has no branch around them.
     const int ntile = a.tile0[a.nseg];
-    TileBlocks tb;
+    TileBlocks tb, tn;
+    int s_tb = 0;
     if (ntile > 0) {
-        const int s = seg_of(a, 0);
-        load_blocks(a, a.seg[s], 0, vrole, t, head, tb);
-        store_blocks(lds, a.seg[s], vrole, t, head, tb);
+        const int s0 = seg_of(a, 0);
+        load_blocks(a, a.seg[s0], 0, t, head, tb);
+        store_blocks(lds, a.seg[s0], t, head, tb);
+        const int j1 = ntile > 1 ? 1 : 0;
+        s_tb = seg_of(a, j1);
+        load_blocks(a, a.seg[s_tb], (j1 - a.tile0[s_tb]) * kAK, t, head, tb);
     }
     __syncthreads();
 
     for (int j = 0; j < ntile; ++j) {
-        const bool more = j + 1 < ntile;
         const int sj = seg_of(a, j);
-        const int sn = more ? seg_of(a, j + 1) : sj;
-        if (more) load_blocks(a, a.seg[sn], (int64_t)(j + 1 - a.tile0[sn]) * kAK, vrole, t, head, tb);
+        const int j2 = j + 2 < ntile ? j + 2 : ntile - 1;
+        const int s2 = seg_of(a, j2);
+        load_blocks(a, a.seg[s2], (j2 - a.tile0[s2]) * kAK, t, head, tn);
 
         const uint8_t *st = lds + (j & 1) * kAStage;
         // S^T = K_hat Q^T: two 32-key blocks, alternating so that no MFMA
@@ -223,20 +246,20 @@ __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
         // keys past the segment's end
         const int64_t nvalid = a.seg[sj].n - (int64_t)(j - a.tile0[sj]) * kAK;
         if (nvalid < kAK) {
+            // key kb*32 + h*4 + (e>>2)*8 + (e&3) against nvalid, the lane's
+            // part moved to the right so each compare takes a constant
+            const int lim = (int)nvalid - h * 4;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int e = 0; e < 16; ++e)
-                    if (kb * 32 + h * 4 + (e >> 2) * 8 + (e & 3) >= nvalid)
-                        sacc[kb][e] = -__builtin_inff();
+                    if (kb * 32 + (e >> 2) * 8 + (e & 3) >= lim) sacc[kb][e] = -__builtin_inff();
         }
         // online softmax
-        float mx = -__builtin_inff();
+        float mx = sacc[0][0];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        for (int e = 1; e < 32; ++e) mx = fmaxf(mx, sacc[e >> 4][e & 15]);
+        mx = half_max(mx);
         const float m_new = fmaxf(m_run, mx * a.scale_log2);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         float ps = 0.0f;
@@ -259,25 +282,27 @@ __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
                 for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
         }
         m_run = m_new;
-        // O^T += V_hat^T P^T
+        // O^T += V_hat^T P^T, the four d blocks in turn (independent MFMAs)
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-            const int d = db * 32 + c;
-            const int sw = ((d >> 1) & 7) ^ ((d >> 4) & 7);
+        for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
+            for (int db = 0; db < 4; ++db) {
+                const int d = db * 32 + c;
+                const int sw = ((d >> 1) & 7) ^ ((d >> 4) & 7);
                 const bf16x8 vf =
                     *(const bf16x8 *)(st + kATile + d * 128 + (((2 * kk + h) ^ sw) * 16));
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, __builtin_bit_cast(bf16x8, pw[kk]),
                                                                 o[db], 0, 0, 0);
             }
         }
-        if (more) store_blocks(lds + ((j + 1) & 1) * kAStage, a.seg[sn], vrole, t, head, tb);
+        store_blocks(lds + ((j + 1) & 1) * kAStage, a.seg[s_tb], t, head, tb);
+        tb = tn;
+        s_tb = s2;
         __syncthreads();
     }
 
     // both lane halves saw every score maximum, so m_run agrees; the sums add
-    const float lt = l_run + __shfl_xor(l_run, 32);
+    const float lt = half_sum(l_run);
     if (qi < a.nq) {
         const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
         uint16_t *op = a.o + qi * a.HD + head * kAD;
