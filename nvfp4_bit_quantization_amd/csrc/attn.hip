@@ -33,8 +33,7 @@
 // kb * 32 + h * 4 + (e >> 2) * 8 + (e & 3) (h = lane >> 5); V^T keeps key k of
 // each 16-key group at column ((k >> 2) & 1) * 8 + ((k >> 3) & 1) * 4 + (k & 3),
 // so the 8 keys of a lane's P^T operand slots are 16 contiguous bytes of V^T.
-// Each wave's queries sit in LDS too (same swizzle as the K tile), read one
-// 16-deep fragment at a time.  The packed blocks of tile j + 2 are loaded
+// Each wave keeps its 32 queries in registers.  The packed blocks of tile j + 2 are loaded
 // during tile j, and tile j + 1 is dequantized into the other stage in the
 // same instruction stream as tile j's value MFMAs; one barrier per tile.
 #include <atomic>
@@ -51,8 +50,7 @@ constexpr int kAQ = 256;                   // queries per workgroup (8 waves)
 constexpr int kAK = 64;                    // keys per tile
 constexpr int kATile = kAK * kAD * 2;      // bytes of the K tile (and of V^T)
 constexpr int kAStage = 2 * kATile;        // K tile, then V^T tile
-constexpr int kAQOff = 2 * kAStage;        // then each wave's 32 queries x 128 d
-constexpr int kALds = kAQOff + kAQ * kAD * 2;  // 128 KB
+constexpr int kALds = 2 * kAStage;         // 64 KB
 
 // Column of V^T that holds key k of a tile.
 __device__ __forceinline__ int vt_col(int k) {
@@ -179,18 +177,15 @@ __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
     const int c = lane & 31, h = lane >> 5;
     const int t = threadIdx.x;
 
-    // the wave's queries (Q^T operand rows) into its LDS region: query
-    // qw + c in row c, 16-byte column x in slot x ^ (c & 15); lane (c, h)
-    // copies columns 2 ks + h
+    // Q^T operand in registers: lane (c, h) holds query qw + c (clamped),
+    // d = 16 ks + 8 h .. + 8
     const int64_t qw = q0 + wave * 32;
     const int64_t qi = qw + c;
-    uint8_t *const qs = lds + kAQOff + wave * (32 * kAD * 2);
+    bf16x8 qf[8];
     {
         const uint16_t *qp = a.q + (qi < a.nq ? qi : a.nq - 1) * a.HD + head * kAD + h * 8;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-            *(u32x4 *)(qs + c * 256 + (((2 * ks + h) ^ (c & 15)) * 16)) =
-                *(const u32x4 *)(qp + ks * 16);
+        for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8 *)(qp + ks * 16);
     }
 
     f32x16 o[4];
@@ -226,8 +221,7 @@ __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
 
         const uint8_t *st = lds + (j & 1) * kAStage;
         // S^T = K_hat Q^T: two 32-key blocks, alternating so that no MFMA
-        // waits for the one before it (keys kb * 32 + c share the swizzle
-        // of query row c)
+        // waits for the one before it
         f32x16 sacc[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -236,11 +230,10 @@ __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             const int col = ((2 * ks + h) ^ (c & 15)) * 16;
-            const bf16x8 qv = *(const bf16x8 *)(qs + c * 256 + col);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 const bf16x8 kf = *(const bf16x8 *)(st + (kb * 32 + c) * 256 + col);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qv, sacc[kb], 0, 0, 0);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[kb], 0, 0, 0);
             }
         }
         // keys past the segment's end
