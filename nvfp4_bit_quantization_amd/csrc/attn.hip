@@ -33,9 +33,10 @@
 // kb * 32 + h * 4 + (e >> 2) * 8 + (e & 3) (h = lane >> 5); V^T keeps key k of
 // each 16-key group at column ((k >> 2) & 1) * 8 + ((k >> 3) & 1) * 4 + (k & 3),
 // so the 8 keys of a lane's P^T operand slots are 16 contiguous bytes of V^T.
-// Each wave keeps its 32 queries in registers.  The packed blocks of tile j + 2 are loaded
-// during tile j, and tile j + 1 is dequantized into the other stage in the
-// same instruction stream as tile j's value MFMAs; one barrier per tile.
+// Each wave keeps its 32 queries in registers.  The packed blocks of tile
+// j + 2 are loaded during tile j, and tile j + 1 is dequantized into the
+// other stage in the same instruction stream as tile j's value MFMAs; one
+// barrier per tile.
 #include <atomic>
 
 #include "device.hpp"
