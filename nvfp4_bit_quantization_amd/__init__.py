@@ -459,6 +459,8 @@ class KVRing:
             softmax_scale = self.cfg.head_dim ** -0.5
         if out is None:
             out = torch.empty_like(q)
+        elif out.dtype != torch.bfloat16 or out.shape != q.shape:
+            raise ValueError("out must be bfloat16 with q's shape")
         if lse is not None and (lse.dtype != torch.float32 or lse.shape != q.shape[:2]):
             raise ValueError("lse must be float32 [n_q, heads]")
         _check(lib().nvfp4_attention_window(

@@ -168,6 +168,10 @@ def test_attention_validation(nv):
         ring.attention(1, q)  # step != next chunk
     with pytest.raises(ValueError):
         ring.attention(0, q[:, :1])  # wrong head count
+    with pytest.raises(ValueError):
+        ring.attention(0, q, out=torch.empty((3, 2, 128), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError):
+        ring.attention(0, q, lse=torch.empty((4, 3), dtype=torch.float32, device="cuda"))
     ring64 = nv.KVRing(small_cfg(nv, head_dim=64))
     with pytest.raises(RuntimeError):
         ring64.attention(0, torch.zeros((4, 2, 64), dtype=torch.bfloat16, device="cuda"))
