@@ -23,6 +23,9 @@
  *      Sink; Italian page, section Multi-Shot Attention Sink.)
  *   4. The W4A4 GEMM on NVFP4 operands.  (DeepRead summary, inference
  *      infrastructure / NVFP4 inference; Italian page, Inferenza W4A4 NVFP4.)
+ * Built on these: the GEMM with its epilogue quantizing the output, the LoRA
+ * branch on the frozen NVFP4 backbone, the RHT quantizer, and attention over
+ * K_eff(t) read packed from the ring (each declared below with its source).
  *
  * Conventions (all entry points):
  *   - Device pointers are HIP device memory owned by the caller; the library
@@ -356,6 +359,7 @@ int nvfp4_gather_window(const nvfp4_kv_ring *ring, int64_t step, void *K_out, vo
  * gathered K/V).  Scores and sums in fp32 (the products on the bf16 MFMA),
  * the softmax weights rounded to bf16 for the value product, o rounded to
  * bf16 (nearest-even).
+ *   softmax_scale: finite and >= 0 (0 gives the mean of the values).
  *   step: must equal ring->next_chunk, as for the gather.
  *   q, o: device bf16 [n_q, H, 128], row-major, 16-byte aligned; head_dim
  *     must be 128 (else NVFP4_ESHAPE).

@@ -239,7 +239,8 @@ __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
         }
         // keys past the segment's end
         const int64_t nvalid = a.seg[sj].n - (int64_t)(j - a.tile0[sj]) * kAK;
-        if (nvalid < kAK) {
+        const bool partial = nvalid < kAK;
+        if (partial) {
             // key kb*32 + h*4 + (e>>2)*8 + (e&3) against nvalid, the lane's
             // part moved to the right so each compare takes a constant
             const int lim = (int)nvalid - h * 4;
@@ -262,8 +263,16 @@ __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int e = 0; e < 16; e += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][e], a.scale_log2, -m_new));
-                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][e + 1], a.scale_log2, -m_new));
+                float x0 = __builtin_fmaf(sacc[kb][e], a.scale_log2, -m_new);
+                float x1 = __builtin_fmaf(sacc[kb][e + 1], a.scale_log2, -m_new);
+                if (partial) {
+                    // a masked key at scale 0 gives -inf * 0 = NaN: maxNum
+                    // turns it back into -inf (weight 0)
+                    x0 = fmaxf(x0, -__builtin_inff());
+                    x1 = fmaxf(x1, -__builtin_inff());
+                }
+                const float p0 = __builtin_amdgcn_exp2f(x0);
+                const float p1 = __builtin_amdgcn_exp2f(x1);
                 ps += p0;
                 ps += p1;
                 pw[kb * 2 + (e >> 3)][(e & 7) >> 1] = pack_bf16x2(p0, p1);

@@ -550,8 +550,8 @@ int nvfp4_attention_window(const nvfp4_kv_ring *ring, int64_t step, const void *
         return fail(NVFP4_ESHAPE, "attention_window: head_dim must be 128 (got %d)",
                     ring->cfg.head_dim);
     if (n_q < 0) return fail(NVFP4_ESHAPE, "attention_window: negative query count");
-    if (!(softmax_scale == softmax_scale) || softmax_scale > 3.0e38f || softmax_scale < -3.0e38f)
-        return fail(NVFP4_EINVAL, "attention_window: softmax_scale must be finite");
+    if (!(softmax_scale >= 0.0f && softmax_scale <= 3.4e38f))
+        return fail(NVFP4_EINVAL, "attention_window: softmax_scale must be finite and >= 0");
     if (n_q > 0 && (!q_bf16 || !o_bf16))
         return fail(NVFP4_EINVAL, "attention_window: NULL q or o");
     if (!aligned16(q_bf16) || !aligned16(o_bf16) || ((uintptr_t)lse & 3u))

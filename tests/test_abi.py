@@ -195,6 +195,7 @@ def test_attention_window_validation(L):
     assert a(nq=-1) == -3
     assert a(scale=float("nan")) == -1
     assert a(scale=float("inf")) == -1
+    assert a(scale=-0.5) == -1
     assert a(q=None) == -1
     assert a(o=None) == -1
     assert a(q=FAKE + 2) == -2

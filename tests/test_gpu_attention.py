@@ -46,11 +46,11 @@ def queries(seed, n, H, d):
     return qb.reshape(n, H, d), f32_of_bits(qb).reshape(n, H, d)
 
 
-def check(nv, orc, ring, chunks, cfg, t, shot, qbits, qf, rows=None):
+def check(nv, orc, ring, chunks, cfg, t, shot, qbits, qf, rows=None, scale=None):
     Tc, H, d = cfg.chunk_tokens, cfg.heads, cfg.head_dim
     g_tok = cfg.sink_frames_global * cfg.tokens_per_frame
     s_tok = cfg.sink_frames_shot * cfg.tokens_per_frame
-    scale = d ** -0.5
+    scale = d ** -0.5 if scale is None else scale
     nq = qf.shape[0]
     lse = torch.empty((nq, H), dtype=torch.float32, device="cuda")
     o = ring.attention(t, bf16_gpu(qbits, (nq, H, d)), scale, lse=lse)
@@ -124,6 +124,21 @@ def test_attention_query_counts(nv, orc, nq):
             check(nv, orc, ring, chunks, cfg, t, shot, qbits, qf)
 
     drive(nv, orc, cfg, {0, 3}, 6, 3004, at)
+
+
+@pytest.mark.parametrize("scale", [0.0, 0.01, 0.3])
+def test_attention_softmax_scales(nv, orc, scale):
+    """Scale 0 (uniform weights: the mean of the values), a flat and a
+    sharp softmax, at a step with all four segments."""
+    cfg = small_cfg(nv)
+    qbits, qf = queries(3007, 70, cfg.heads, cfg.head_dim)
+
+    def at(ring, chunks, t, shot):
+        if t == 7:  # global sink, shot sink (chunk 4, below the window), chunks 5 and 6
+            print("case: attention scale", scale, flush=True)
+            check(nv, orc, ring, chunks, cfg, t, shot, qbits, qf, scale=scale)
+
+    drive(nv, orc, cfg, {0, 4}, 8, 3008, at)
 
 
 def test_attention_64s_ring_step_15_sampled(nv, orc):
