@@ -83,13 +83,14 @@ def check_against_oracle(nv, orc, qa, qw, w_layout, amax, search, rows=None):
                                             (256, 208, 512, 0), (33, 16, 256, 1)],
                          ids=["lds_path", "general_path", "w_1d", "tiny"])
 @pytest.mark.parametrize("search", [1, 0], ids=["4o6", "6only"])
-@pytest.mark.parametrize("amax_mode", ["exact", "stale", "headroom"])
+@pytest.mark.parametrize("amax_mode", ["exact", "stale", "headroom", "zero"])
 def test_gemm_quant_exact_vs_oracle(nv, orc, M, N, K, w_layout, search, amax_mode):
     print("case: gemm_quant exact", M, N, K, w_layout, search, amax_mode, flush=True)
     qa, qw = exact_operands(2001, M, N, K, w_layout)
     y_ref, _ = orc.gemm_ref(*qa, *qw, w_layout=w_layout)
     true_amax = float(np.abs(bf16_of(orc, y_ref)).max())
-    amax = {"exact": true_amax, "stale": 0.5 * true_amax, "headroom": 3.0 * true_amax}[amax_mode]
+    amax = {"exact": true_amax, "stale": 0.5 * true_amax, "headroom": 3.0 * true_amax,
+            "zero": 0.0}[amax_mode]  # zero: tensor scales 1 and 1, large values saturate
     check_against_oracle(nv, orc, qa, qw, w_layout, amax, search)
 
 
