@@ -37,8 +37,6 @@
 // j + 2 are loaded during tile j, and tile j + 1 is dequantized into the
 // other stage in the same instruction stream as tile j's value MFMAs; one
 // barrier per tile.
-#include <atomic>
-
 #include "device.hpp"
 #include "launch.hpp"
 

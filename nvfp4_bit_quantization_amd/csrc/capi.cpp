@@ -538,6 +538,9 @@ int nvfp4_gather_window(const nvfp4_kv_ring *ring, int64_t step, void *K_out, vo
     return hip_status(e, "gather_window launch");
 }
 
+static_assert(nvfp4::kAttnMaxSeg >= 2 + NVFP4_KV_MAX_WINDOW,
+              "attention segments: two sinks and every window chunk");
+
 int nvfp4_attention_window(const nvfp4_kv_ring *ring, int64_t step, const void *q_bf16,
                            int64_t n_q, float softmax_scale, void *o_bf16, float *lse,
                            void *stream) {
