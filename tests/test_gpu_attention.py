@@ -175,6 +175,24 @@ def test_attention_64s_ring_step_15_sampled(nv, orc):
     check(nv, orc, ring, chunks, cfg, 15, 10, qbits, qf, rows=rows)
 
 
+def test_attention_deterministic(nv, orc):
+    """Fixed tile order and fixed in-tile order: two calls agree bit for bit."""
+    cfg = small_cfg(nv)
+    qbits, _ = queries(3009, 300, cfg.heads, cfg.head_dim)
+
+    def at(ring, chunks, t, shot):
+        if t == 7:
+            q = bf16_gpu(qbits, (300, cfg.heads, cfg.head_dim))
+            l1 = torch.empty((300, cfg.heads), dtype=torch.float32, device="cuda")
+            l2 = torch.empty_like(l1)
+            o1 = ring.attention(t, q, lse=l1)
+            o2 = ring.attention(t, q, lse=l2)
+            torch.cuda.synchronize()
+            assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+    drive(nv, orc, cfg, {0, 4}, 8, 3010, at)
+
+
 def test_attention_validation(nv):
     cfg = small_cfg(nv)
     ring = nv.KVRing(cfg)
