@@ -226,13 +226,24 @@ __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.0f;
+        {
+            // fragment reads four MFMAs ahead of their use
+            constexpr int PF = 4;
+            bf16x8 kf[PF];
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const int col = ((2 * ks + h) ^ (c & 15)) * 16;
+            for (int i = 0; i < PF; ++i) {
+                const int ks = i >> 1, kb = i & 1;
+                kf[i] = *(const bf16x8 *)(st + (kb * 32 + c) * 256 + (((2 * ks + h) ^ (c & 15)) * 16));
+            }
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 kf = *(const bf16x8 *)(st + (kb * 32 + c) * 256 + col);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[kb], 0, 0, 0);
+            for (int i = 0; i < 16; ++i) {
+                const int ks = i >> 1, kb = i & 1;
+                const bf16x8 cur = kf[i % PF];
+                if (i + PF < 16) {
+                    const int ks2 = (i + PF) >> 1, kb2 = (i + PF) & 1;
+                    kf[i % PF] = *(const bf16x8 *)(st + (kb2 * 32 + c) * 256 + (((2 * ks2 + h) ^ (c & 15)) * 16));
+                }
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[ks], sacc[kb], 0, 0, 0);
             }
         }
         // keys past the segment's end
@@ -284,15 +295,24 @@ __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
         }
         m_run = m_new;
         // O^T += V_hat^T P^T, the four d blocks in turn (independent MFMAs)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
+        {
+            // fragment reads four MFMAs ahead of their use
+            constexpr int PF = 4;
+            auto vaddr = [&](int i) {
+                const int kk = i >> 2, db = i & 3;
                 const int d = db * 32 + c;
                 const int sw = ((d >> 1) & 7) ^ ((d >> 4) & 7);
-                const bf16x8 vf =
-                    *(const bf16x8 *)(st + kATile + d * 128 + (((2 * kk + h) ^ sw) * 16));
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, __builtin_bit_cast(bf16x8, pw[kk]),
+                return (const bf16x8 *)(st + kATile + d * 128 + (((2 * kk + h) ^ sw) * 16));
+            };
+            bf16x8 vf[PF];
+#pragma unroll
+            for (int i = 0; i < PF; ++i) vf[i] = *vaddr(i);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int kk = i >> 2, db = i & 3;
+                const bf16x8 cur = vf[i % PF];
+                if (i + PF < 16) vf[i % PF] = *vaddr(i + PF);
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, __builtin_bit_cast(bf16x8, pw[kk]),
                                                                 o[db], 0, 0, 0);
             }
         }
