@@ -357,8 +357,9 @@ int nvfp4_gather_window(const nvfp4_kv_ring *ring, int64_t step, void *K_out, vo
  * over the tokens j of K_eff(step), with K_hat and V_hat the bf16 values
  * nvfp4_gather_window would write (so the result equals attention over the
  * gathered K/V).  Scores and sums in fp32 (the products on the bf16 MFMA),
- * the softmax weights rounded to bf16 for the value product, o rounded to
- * bf16 (nearest-even).
+ * the softmax weights rounded to bf16 for the value product and its
+ * normaliser alike (so exp(lse) carries their 2^-9 relative rounding), o
+ * rounded to bf16 (nearest-even).
  *   softmax_scale: finite and >= 0 (0 gives the mean of the values).
  *   step: must equal ring->next_chunk, as for the gather.
  *   q, o: device bf16 [n_q, H, 128], row-major, 16-byte aligned; head_dim

@@ -28,7 +28,8 @@
 // the 64 banks.  Per tile and wave: S^T = K_hat Q^T on
 // v_mfma_f32_32x32x16_bf16 (a lane holds one query and 32 of the tile's
 // scores), the online softmax in registers (exp2 of the scores times
-// scale * log2 e), P^T rounded to bf16, O^T += V_hat^T P^T.  A lane of the
+// scale * log2 e), P^T rounded to bf16, O^T += V_hat^T P^T; the normaliser
+// sums the same bf16 weights (v_dot2_f32_bf16 against ones, two a step).  A lane of the
 // 32x32 accumulator holds, for key block kb and element e, key
 // kb * 32 + h * 4 + (e >> 2) * 8 + (e & 3) (h = lane >> 5); V^T keeps key k of
 // each 16-key group at column ((k >> 2) & 1) * 8 + ((k >> 3) & 1) * 4 + (k & 3),
@@ -267,6 +268,7 @@ __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
         const float m_new = fmaxf(m_run, mx * a.scale_log2);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         float ps = 0.0f;
+        const bf16x2 ones2 = __builtin_bit_cast(bf16x2, 0x3F803F80u);
         u32x4 pw[4];  // P^T operands: bf16 pairs
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -282,9 +284,9 @@ __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
                 }
                 const float p0 = __builtin_amdgcn_exp2f(x0);
                 const float p1 = __builtin_amdgcn_exp2f(x1);
-                ps += p0;
-                ps += p1;
-                pw[kb * 2 + (e >> 3)][(e & 7) >> 1] = pack_bf16x2(p0, p1);
+                const uint32_t w = pack_bf16x2(p0, p1);
+                pw[kb * 2 + (e >> 3)][(e & 7) >> 1] = w;
+                ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones2, ps, false);
             }
         l_run = __builtin_fmaf(l_run, alpha, ps);
         if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
