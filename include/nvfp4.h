@@ -366,11 +366,44 @@ int nvfp4_gather_window(const nvfp4_kv_ring *ring, int64_t step, void *K_out, vo
  *     must be 128 (else NVFP4_ESHAPE).
  *   lse: NULL, or device fp32 [n_q, H] (for merging with attention over
  *     other keys, e.g. the chunk's own).
- *   An empty K_eff (step 0) gives o = 0 and lse = -inf.  One kernel launch.
+ *   key_splits: 0 lets the library choose (see nvfp4_attention_plan), 1 to
+ *     NVFP4_ATTN_MAX_SPLITS fixes the count (else NVFP4_EINVAL).  With s > 1
+ *     splits the key set's 64-key tiles are cut into s consecutive runs of
+ *     near-equal length, each run's partial softmax (fp32 unnormalised output,
+ *     running maximum and sum of weights) goes to the workspace, and a second
+ *     kernel combines the runs in index order, rescaling each by 2^(m_s - M)
+ *     (the blockwise softmax merge).  Results depend on s only through fp32
+ *     rounding and are identical from call to call for the same s.
+ *   ws, ws_bytes: device workspace of at least the bytes nvfp4_attention_plan
+ *     reports for the same arguments, 256-byte aligned (else NVFP4_ENOSPC /
+ *     NVFP4_EALIGN); unused (may be NULL) when the plan has one split.  Owned
+ *     by the caller; the call must not overlap another use of it.
+ *   An empty K_eff (step 0) gives o = 0 and lse = -inf.  One kernel launch,
+ *   two with splits.
  */
 int nvfp4_attention_window(const nvfp4_kv_ring *ring, int64_t step, const void *q_bf16,
                            int64_t n_q, float softmax_scale, void *o_bf16, float *lse,
-                           void *stream);
+                           int32_t key_splits, void *ws, size_t ws_bytes, void *stream);
+
+#define NVFP4_ATTN_MAX_SPLITS 8
+
+/*
+ * Key splits and workspace bytes nvfp4_attention_window takes for the same
+ * ring, step, n_q and key_splits (same checks, same errors; host only, but
+ * key_splits = 0 reads the current device's compute-unit count).  The
+ * automatic choice: a workgroup of 256 queries of one head fills a compute
+ * unit, so n = ceil(n_q / 256) * H workgroups run in rounds of one per
+ * unit, and s splits take ceil(n s / CUs) rounds of 1/s the time, each split
+ * adding about 1.5% (its pipeline fill, its partial output, the merge).  The
+ * cheapest s in 1..8 under that model is taken if it saves 3% over one
+ * split, each split keeping at least 8 of the 64-key tiles (e.g. 7040 queries
+ * x 24 heads on 256 units: 672 workgroups, 3 splits, 8 rounds of a third
+ * instead of 3 whole ones; 256 queries x 24 heads: 8 splits).
+ * Workspace: the (max, sum) fp32 pairs, 8 s n_q H bytes rounded up to a
+ * multiple of 256, then the fp32 outputs, 512 s n_q H bytes; 0 for one split.
+ */
+int nvfp4_attention_plan(const nvfp4_kv_ring *ring, int64_t step, int64_t n_q, int32_t key_splits,
+                         int32_t *splits, size_t *ws_bytes);
 
 /* ------------------------------------------------------------------------ */
 /* Kernel timing                                                              */

@@ -97,7 +97,10 @@ _EXPORTS = {
     "nvfp4_gather_window": ([C.POINTER(CKvRing), C.c_int64, C.c_void_p, C.c_void_p, C.c_int64,
                              C.POINTER(C.c_int64), C.c_void_p], C.c_int),
     "nvfp4_attention_window": ([C.POINTER(CKvRing), C.c_int64, C.c_void_p, C.c_int64, C.c_float,
-                                C.c_void_p, C.c_void_p, C.c_void_p], C.c_int),
+                                C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t,
+                                C.c_void_p], C.c_int),
+    "nvfp4_attention_plan": ([C.POINTER(CKvRing), C.c_int64, C.c_int64, C.c_int32,
+                              C.POINTER(C.c_int32), C.POINTER(C.c_size_t)], C.c_int),
     "nvfp4_profile_enable": ([C.c_int], C.c_int),
     "nvfp4_profile_collect": ([C.c_char_p, C.c_int, C.c_void_p, C.c_void_p, C.c_int], C.c_int),
 }
@@ -445,13 +448,24 @@ class KVRing:
                                          _stream(stream)))
         return K_out[:got.value], V_out[:got.value]
 
+    def attention_plan(self, step: int, n_q: int, key_splits: int = 0) -> tuple[int, int]:
+        """nvfp4_attention_plan: (key splits, workspace bytes) of attention()
+        with these arguments (key_splits 0 = the library's choice)."""
+        sp, wsb = C.c_int32(), C.c_size_t()
+        _check(lib().nvfp4_attention_plan(C.byref(self.ring), step, n_q, key_splits,
+                                          C.byref(sp), C.byref(wsb)))
+        return sp.value, wsb.value
+
     def attention(self, step: int, q: torch.Tensor, softmax_scale: float | None = None,
                   out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                  key_splits: int = 0, workspace: torch.Tensor | None = None,
                   stream=None) -> torch.Tensor:
         """nvfp4_attention_window: attention of q (bf16 [n_q, heads, 128]) over
         K_eff(step), read packed from the ring.  softmax_scale defaults to
         1/sqrt(head_dim); lse (optional float32 [n_q, heads]) receives the
-        log-sum-exp of the scaled scores."""
+        log-sum-exp of the scaled scores.  key_splits: 0 = the library's
+        choice, else 1..8; the workspace the splits need is allocated here
+        unless `workspace` (uint8, on q's device) is given."""
         if q.dtype != torch.bfloat16 or q.dim() != 3 or q.shape[1:] != (self.cfg.heads,
                                                                         self.cfg.head_dim):
             raise ValueError(f"q must be bfloat16 [n_q, {self.cfg.heads}, {self.cfg.head_dim}]")
@@ -463,9 +477,18 @@ class KVRing:
             raise ValueError("out must be bfloat16 with q's shape")
         if lse is not None and (lse.dtype != torch.float32 or lse.shape != q.shape[:2]):
             raise ValueError("lse must be float32 [n_q, heads]")
+        _, wsb = self.attention_plan(step, q.shape[0], key_splits)
+        ws = None
+        if wsb > 0:
+            if workspace is None:
+                workspace = torch.empty(wsb, dtype=torch.uint8, device=q.device)
+            elif workspace.dtype != torch.uint8 or workspace.numel() < wsb:
+                raise ValueError(f"workspace must be uint8 with at least {wsb} elements")
+            ws = _dev(workspace, "workspace")
         _check(lib().nvfp4_attention_window(
             C.byref(self.ring), step, _dev(q, "q"), q.shape[0], float(softmax_scale),
-            _dev(out, "out"), None if lse is None else _dev(lse, "lse"), _stream(stream)))
+            _dev(out, "out"), None if lse is None else _dev(lse, "lse"), key_splits, ws,
+            workspace.numel() if wsb > 0 else 0, _stream(stream)))
         return out
 
 

@@ -163,13 +163,15 @@ __device__ __forceinline__ float half_sum(float v) {
 
 __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    // workgroups of one head run on one XCD (b % 8), sharing its L2
+    // workgroups of one (split, head) run on one XCD (b % 8), sharing its L2
     const int64_t nqt = (a.nq + kAQ - 1) / kAQ;
-    const int64_t total = nqt * a.heads;
+    const int64_t units = nqt * a.heads;
+    const int64_t total = units * a.nsplit;
     const int64_t bid = blockIdx.x;
     const int64_t per = total / 8;
     const int64_t tix = bid < per * 8 ? (bid % 8) * per + bid / 8 : bid;
-    const int head = (int)(tix / nqt);
+    const int split = (int)(tix / units);
+    const int head = (int)(tix % units / nqt);
     const int64_t q0 = (tix % nqt) * kAQ;
 
     const int lane = threadIdx.x & 63;
@@ -195,31 +197,33 @@ __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
         for (int e = 0; e < 16; ++e) o[db][e] = 0.0f;
     float m_run = -__builtin_inff(), l_run = 0.0f;
 
-    // Tile j + 1's blocks (tb, segment s_tb) were loaded one iteration
-    // earlier and are dequantized into the idle stage among tile j's value
-    // MFMAs; tile j + 2's are requested at the top of iteration j.  Past the
-    // last tile the loads repeat it and the extra stage write is never read,
-    // so the loop has no branch around them.
+    // The split's tiles [jb, je).  Tile j + 1's blocks (tb, segment s_tb)
+    // were loaded one iteration earlier and are dequantized into the idle
+    // stage among tile j's value MFMAs; tile j + 2's are requested at the
+    // top of iteration j.  Past the last tile the loads repeat it and the
+    // extra stage write is never read, so the loop has no branch around them.
     const int ntile = a.tile0[a.nseg];
+    const int jb = (int)((int64_t)split * ntile / a.nsplit);
+    const int je = (int)((int64_t)(split + 1) * ntile / a.nsplit);
     TileBlocks tb, tn;
     int s_tb = 0;
-    if (ntile > 0) {
-        const int s0 = seg_of(a, 0);
-        load_blocks(a, a.seg[s0], 0, t, head, tb);
+    if (je > jb) {
+        const int s0 = seg_of(a, jb);
+        load_blocks(a, a.seg[s0], (jb - a.tile0[s0]) * kAK, t, head, tb);
         store_blocks(lds, a.seg[s0], t, head, tb);
-        const int j1 = ntile > 1 ? 1 : 0;
+        const int j1 = jb + 1 < je ? jb + 1 : jb;
         s_tb = seg_of(a, j1);
         load_blocks(a, a.seg[s_tb], (j1 - a.tile0[s_tb]) * kAK, t, head, tb);
     }
     __syncthreads();
 
-    for (int j = 0; j < ntile; ++j) {
+    for (int j = jb; j < je; ++j) {
         const int sj = seg_of(a, j);
-        const int j2 = j + 2 < ntile ? j + 2 : ntile - 1;
+        const int j2 = j + 2 < je ? j + 2 : je - 1;
         const int s2 = seg_of(a, j2);
         load_blocks(a, a.seg[s2], (j2 - a.tile0[s2]) * kAK, t, head, tn);
 
-        const uint8_t *st = lds + (j & 1) * kAStage;
+        const uint8_t *st = lds + ((j - jb) & 1) * kAStage;
         // S^T = K_hat Q^T: two 32-key blocks, alternating so that no MFMA
         // waits for the one before it
         f32x16 sacc[2];
@@ -318,7 +322,7 @@ __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
                                                                 o[db], 0, 0, 0);
             }
         }
-        store_blocks(lds + ((j + 1) & 1) * kAStage, a.seg[s_tb], t, head, tb);
+        store_blocks(lds + ((j - jb + 1) & 1) * kAStage, a.seg[s_tb], t, head, tb);
         tb = tn;
         s_tb = s2;
         __syncthreads();
@@ -326,6 +330,21 @@ __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
 
     // both lane halves saw every score maximum, so m_run agrees; the sums add
     const float lt = half_sum(l_run);
+    if (a.nsplit > 1) {
+        // the split's share: unnormalised output and (max, sum of weights)
+        if (qi < a.nq) {
+            const int64_t r = ((int64_t)split * a.nq + qi) * a.heads + head;
+            float *po = a.part_o + r * kAD;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *(f32x4 *)(po + db * 32 + h * 4 + g * 8) =
+                        f32x4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
+            if (h == 0) *(f32x2 *)(a.part_ml + 2 * r) = f32x2{m_run, lt};
+        }
+        return;
+    }
     if (qi < a.nq) {
         const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
         uint16_t *op = a.o + qi * a.HD + head * kAD;
@@ -344,14 +363,103 @@ __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
     }
 }
 
+// Merge of the key splits: thread (query, head, 8 d).  With M the largest
+// split maximum and w_s = 2^(m_s - M), o = sum_s w_s o_s / sum_s w_s l_s and
+// lse = (M + log2 sum_s w_s l_s) ln 2, splits in index order; a split
+// without keys has m = -inf and l = 0, and no keys at all give o = 0 and
+// lse = -inf as in the single-split kernel.
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+    const int64_t nqh = a.nq * a.heads;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= nqh * 16) return;
+    const int64_t r = i >> 4;
+    const int g = (int)(i & 15);
+    float M = -__builtin_inff();
+    for (int sp = 0; sp < a.nsplit; ++sp) M = fmaxf(M, a.part_ml[2 * (sp * nqh + r)]);
+    float L = 0.0f;
+    f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
+    if (M != -__builtin_inff()) {
+        for (int sp = 0; sp < a.nsplit; ++sp) {
+            const f32x2 ml = *(const f32x2 *)(a.part_ml + 2 * (sp * nqh + r));
+            const float w = __builtin_amdgcn_exp2f(ml.x - M);
+            const float *po = a.part_o + (sp * nqh + r) * kAD + g * 8;
+            L = __builtin_fmaf(w, ml.y, L);
+            acc0 = w * *(const f32x4 *)po + acc0;
+            acc1 = w * *(const f32x4 *)(po + 4) + acc1;
+        }
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    *(u32x4 *)(a.o + r * kAD + g * 8) =
+        u32x4{pack_bf16x2(acc0.x * inv, acc0.y * inv), pack_bf16x2(acc0.z * inv, acc0.w * inv),
+              pack_bf16x2(acc1.x * inv, acc1.y * inv), pack_bf16x2(acc1.z * inv, acc1.w * inv)};
+    if (a.lse && g == 0)
+        a.lse[r] = L > 0.0f ? (M + log2f(L)) * 0.69314718055994531f : -__builtin_inff();
+}
+
+size_t attn_workspace_bytes(int64_t nq, int heads, int nsplit) {
+    if (nsplit <= 1) return 0;
+    const size_t rows = (size_t)nsplit * (size_t)nq * (size_t)heads;
+    return (rows * 8 + 255) / 256 * 256 + rows * kAD * 4;
+}
+
+// Compute units of each device, read once.
+static int device_cus(int dev, hipError_t &e) {
+    static std::atomic<int> cache[64];
+    e = hipSuccess;
+    if (dev >= 0 && dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || n <= 0) return 0;
+    if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// One 8-wave workgroup fills a compute unit (two waves a SIMD at the
+// kernel's register count), so a launch runs in rounds of `cus` workgroups.
+// A split count s costs ceil(units * s / cus) rounds of 1/s of a unit's
+// time, times 1 + 0.015 s for what each split adds (its pipeline fill and
+// partial output, the merge; measured ~1.5% a split on 7040 queries x 24
+// heads over 33,440 keys).  The cheapest s is taken if it saves 3% over one
+// split, each split keeping at least 8 tiles.
+hipError_t attn_choose_splits(int64_t nq, int heads, int ntile, int requested, int *nsplit) {
+    if (requested > 0) {
+        *nsplit = requested;
+        return hipSuccess;
+    }
+    *nsplit = 1;
+    const int64_t units = (nq + kAQ - 1) / kAQ * heads;
+    if (units == 0 || ntile < 16) return hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const int cus = device_cus(dev, e);
+    if (e != hipSuccess) return e;
+    if (cus <= 0) return hipSuccess;
+    auto cost = [&](int sp) {
+        return (double)((units * sp + cus - 1) / cus) / sp * (1.0 + 0.015 * sp);
+    };
+    int best = 1;
+    for (int sp = 2; sp <= kAttnMaxSplit && ntile >= 8 * sp; ++sp)
+        if (cost(sp) < cost(best)) best = sp;
+    if (cost(best) <= 0.97 * cost(1)) *nsplit = best;
+    return hipSuccess;
+}
+
 hipError_t launch_attn_window(const AttnArgs &a, hipStream_t s) {
     if (a.nq == 0) return hipSuccess;
     static std::atomic<uint32_t> lds_set{0};
     const void *fn = (const void *)attn_window_kernel;
     hipError_t e = lds_limit_once(&fn, 1, kALds, lds_set);
     if (e != hipSuccess) return e;
-    const int64_t grid = ((a.nq + kAQ - 1) / kAQ) * a.heads;
+    const int64_t grid = ((a.nq + kAQ - 1) / kAQ) * a.heads * a.nsplit;
     NVFP4_LAUNCH("attn_window", attn_window_kernel, dim3((unsigned)grid), dim3(512), kALds, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess || a.nsplit <= 1) return e;
+    const int64_t mgrid = (a.nq * a.heads * 16 + 255) / 256;
+    NVFP4_LAUNCH("attn_merge", attn_merge_kernel, dim3((unsigned)mgrid), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

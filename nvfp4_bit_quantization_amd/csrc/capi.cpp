@@ -538,33 +538,31 @@ int nvfp4_gather_window(const nvfp4_kv_ring *ring, int64_t step, void *K_out, vo
     return hip_status(e, "gather_window launch");
 }
 
+static_assert(nvfp4::kAttnMaxSplit == NVFP4_ATTN_MAX_SPLITS, "attention key splits");
 static_assert(nvfp4::kAttnMaxSeg >= 2 + NVFP4_KV_MAX_WINDOW,
               "attention segments: two sinks and every window chunk");
 
-int nvfp4_attention_window(const nvfp4_kv_ring *ring, int64_t step, const void *q_bf16,
-                           int64_t n_q, float softmax_scale, void *o_bf16, float *lse,
-                           void *stream) {
+// Host checks shared by the plan and the call, and the effective set as
+// segments (ascending token order, the gather's segments).
+static int attn_setup(const nvfp4_kv_ring *ring, int64_t step, int64_t n_q, int32_t key_splits,
+                      const char *who, nvfp4::AttnArgs &a) {
     int st = check_ring(ring);
     if (st) return st;
     if (step != ring->next_chunk)
-        return fail(NVFP4_ESTATE, "attention_window: step %lld != next chunk %lld",
-                    (long long)step, (long long)ring->next_chunk);
+        return fail(NVFP4_ESTATE, "%s: step %lld != next chunk %lld", who, (long long)step,
+                    (long long)ring->next_chunk);
     if (ring->cfg.head_dim != 128)
-        return fail(NVFP4_ESHAPE, "attention_window: head_dim must be 128 (got %d)",
-                    ring->cfg.head_dim);
-    if (n_q < 0) return fail(NVFP4_ESHAPE, "attention_window: negative query count");
-    if (!(softmax_scale >= 0.0f && softmax_scale <= 3.4e38f))
-        return fail(NVFP4_EINVAL, "attention_window: softmax_scale must be finite and >= 0");
-    if (n_q > 0 && (!q_bf16 || !o_bf16))
-        return fail(NVFP4_EINVAL, "attention_window: NULL q or o");
-    if (!aligned16(q_bf16) || !aligned16(o_bf16) || ((uintptr_t)lse & 3u))
-        return fail(NVFP4_EALIGN, "attention_window: q and o must be 16-byte aligned, lse 4");
-    if ((n_q + 255) / 256 * (int64_t)ring->cfg.heads >= ((int64_t)1 << 31))
-        return fail(NVFP4_ESHAPE, "attention_window: too many queries");
+        return fail(NVFP4_ESHAPE, "%s: head_dim must be 128 (got %d)", who, ring->cfg.head_dim);
+    if (n_q < 0) return fail(NVFP4_ESHAPE, "%s: negative query count", who);
+    if (key_splits < 0 || key_splits > nvfp4::kAttnMaxSplit)
+        return fail(NVFP4_EINVAL, "%s: key_splits must be 0 (automatic) or 1..%d (got %d)", who,
+                    nvfp4::kAttnMaxSplit, key_splits);
+    if ((n_q + 255) / 256 * (int64_t)ring->cfg.heads * nvfp4::kAttnMaxSplit >= ((int64_t)1 << 31))
+        return fail(NVFP4_ESHAPE, "%s: too many queries", who);
     const Plan p = plan_effective(ring, step);
     const nvfp4_kv_config &c = ring->cfg;
     const int64_t T = ring->chunk_tokens, hd = ring->hd;
-    nvfp4::AttnArgs a{};
+    a = nvfp4::AttnArgs{};
     int ns = 0;
     auto add = [&](const nvfp4::KvRegion &r, int64_t skip, int64_t n) {
         nvfp4::AttnSeg &s = a.seg[ns++];
@@ -576,7 +574,6 @@ int nvfp4_attention_window(const nvfp4_kv_ring *ring, int64_t step, const void *
         s.sd = r.sd;
         s.n = n;
     };
-    // the same segments as the gather, in ascending token order
     if (p.n_g > 0)
         add(region_at(ring->base + ring->gsink_offset,
                       region_layout((int64_t)c.sink_frames_global * c.tokens_per_frame, hd)),
@@ -597,6 +594,45 @@ int nvfp4_attention_window(const nvfp4_kv_ring *ring, int64_t step, const void *
     a.heads = c.heads;
     a.HD = hd;
     a.nq = n_q;
+    hipError_t e =
+        nvfp4::attn_choose_splits(n_q, c.heads, a.tile0[ns], key_splits, &a.nsplit);
+    return hip_status(e, "attention: device query");
+}
+
+int nvfp4_attention_plan(const nvfp4_kv_ring *ring, int64_t step, int64_t n_q, int32_t key_splits,
+                         int32_t *splits, size_t *ws_bytes) {
+    if (!splits || !ws_bytes) return fail(NVFP4_EINVAL, "attention_plan: NULL output");
+    nvfp4::AttnArgs a;
+    const int st = attn_setup(ring, step, n_q, key_splits, "attention_plan", a);
+    if (st) return st;
+    *splits = a.nsplit;
+    *ws_bytes = nvfp4::attn_workspace_bytes(n_q, a.heads, a.nsplit);
+    return NVFP4_OK;
+}
+
+int nvfp4_attention_window(const nvfp4_kv_ring *ring, int64_t step, const void *q_bf16,
+                           int64_t n_q, float softmax_scale, void *o_bf16, float *lse,
+                           int32_t key_splits, void *ws, size_t ws_bytes, void *stream) {
+    if (!(softmax_scale >= 0.0f && softmax_scale <= 3.4e38f))
+        return fail(NVFP4_EINVAL, "attention_window: softmax_scale must be finite and >= 0");
+    if (n_q > 0 && (!q_bf16 || !o_bf16))
+        return fail(NVFP4_EINVAL, "attention_window: NULL q or o");
+    if (!aligned16(q_bf16) || !aligned16(o_bf16) || ((uintptr_t)lse & 3u))
+        return fail(NVFP4_EALIGN, "attention_window: q and o must be 16-byte aligned, lse 4");
+    nvfp4::AttnArgs a;
+    const int st = attn_setup(ring, step, n_q, key_splits, "attention_window", a);
+    if (st) return st;
+    const size_t need = nvfp4::attn_workspace_bytes(n_q, a.heads, a.nsplit);
+    if (need > 0) {
+        if (!ws || ws_bytes < need)
+            return fail(NVFP4_ENOSPC, "attention_window: %d key splits need %zu workspace bytes (got %zu)",
+                        a.nsplit, need, ws ? ws_bytes : (size_t)0);
+        if ((uintptr_t)ws & 255u)
+            return fail(NVFP4_EALIGN, "attention_window: workspace must be 256-byte aligned");
+        const size_t rows = (size_t)a.nsplit * (size_t)n_q * (size_t)a.heads;
+        a.part_ml = (float *)ws;
+        a.part_o = (float *)((uint8_t *)ws + (rows * 8 + 255) / 256 * 256);
+    }
     a.q = (const uint16_t *)q_bf16;
     a.o = (uint16_t *)o_bf16;
     a.lse = lse;

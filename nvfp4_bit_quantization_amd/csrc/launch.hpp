@@ -112,7 +112,20 @@ struct AttnArgs {
     uint16_t *o;                     // [nq, heads, 128] bf16
     float *lse;                      // [nq, heads] or nullptr
     float scale_log2;                // softmax scale * log2(e)
+    // Key splits: workgroup (split, query block, head) takes the split's
+    // share of the tiles; with nsplit > 1 it writes its unnormalised output
+    // and (running max in log2 units, sum of weights) to the workspace and a
+    // second kernel merges the splits into o and lse.
+    int32_t nsplit;
+    float *part_ml;                  // [nsplit][nq][heads] (m, l)
+    float *part_o;                   // [nsplit][nq][heads][128]
 };
+constexpr int kAttnMaxSplit = 8;      // most key splits a call takes
+// Workspace bytes of `nsplit` key splits (0 for one split).
+size_t attn_workspace_bytes(int64_t nq, int heads, int nsplit);
+// Key splits for nq queries over ntile 64-key tiles: `requested` if > 0,
+// else the count that best fills the device's compute units.
+hipError_t attn_choose_splits(int64_t nq, int heads, int ntile, int requested, int *nsplit);
 hipError_t launch_attn_window(const AttnArgs &a, hipStream_t s);
 
 // ---- gemm.hip

@@ -185,12 +185,14 @@ def test_ring_validation(L):
 
 
 def test_attention_window_validation(L):
-    # nvfp4_attention_window(ring, step, q, n_q, scale, o, lse, stream): every
-    # call below is rejected on the host before a launch
+    # nvfp4_attention_window(ring, step, q, n_q, scale, o, lse, key_splits,
+    # ws, ws_bytes, stream): every call below is rejected on the host before
+    # a launch
     r = make_ring(L)
     a = lambda **kw: L.nvfp4_attention_window(
         C.byref(kw.get("ring", r)), kw.get("step", 0), kw.get("q", FAKE), kw.get("nq", 64),
-        kw.get("scale", 0.088), kw.get("o", FAKE), kw.get("lse", None), None)
+        kw.get("scale", 0.088), kw.get("o", FAKE), kw.get("lse", None), kw.get("splits", 1),
+        kw.get("ws", None), kw.get("wsb", 0), None)
     assert a(step=1) == -5                         # not the next chunk
     assert a(nq=-1) == -3
     assert a(scale=float("nan")) == -1
@@ -200,12 +202,36 @@ def test_attention_window_validation(L):
     assert a(o=None) == -1
     assert a(q=FAKE + 2) == -2
     assert a(lse=FAKE + 1) == -2
+    assert a(splits=-1) == -1 and a(splits=9) == -1
+    assert a(splits=2) == -4                       # two splits need a workspace
+    need = 64 * 24 * 2 * 8 + 64 * 24 * 2 * 512    # (max, sum) block is a multiple of 256
+    assert a(splits=2, ws=FAKE, wsb=need - 1) == -4
+    assert a(splits=2, ws=FAKE + 16, wsb=need) == -2
     c64 = nv.KVConfig(head_dim=64).c()
     r64 = nv.CKvRing()
     assert L.nvfp4_kv_ring_init(C.byref(r64), C.byref(c64), FAKE,
                                 L.nvfp4_kv_ring_bytes(C.byref(c64))) == 0
     assert a(ring=r64) == -3                       # head_dim must be 128
     assert b"128" in L.nvfp4_last_error()
+
+
+def test_attention_plan(L):
+    """Forced split counts and their workspace size need no device; the
+    automatic choice below 8 tiles takes one split without asking it."""
+    r = make_ring(L)
+    sp, wsb = C.c_int32(), C.c_size_t()
+    plan = lambda step, nq, ks: L.nvfp4_attention_plan(C.byref(r), step, nq, ks, C.byref(sp),
+                                                       C.byref(wsb))
+    assert plan(0, 7040, 0) == 0 and (sp.value, wsb.value) == (1, 0)   # empty set
+    assert plan(0, 7040, 1) == 0 and (sp.value, wsb.value) == (1, 0)
+    rows = 3 * 100 * 24
+    assert plan(0, 100, 3) == 0 and sp.value == 3
+    assert wsb.value == (rows * 8 + 255) // 256 * 256 + rows * 512
+    assert plan(0, 100, 8) == 0 and sp.value == 8
+    assert plan(0, 100, 9) == -1 and plan(0, 100, -1) == -1
+    assert plan(1, 100, 2) == -5
+    assert plan(0, -1, 2) == -3
+    assert L.nvfp4_attention_plan(C.byref(r), 0, 100, 2, None, C.byref(wsb)) == -1
 
 
 def test_ring_plan_matches_oracle(L, orc):

@@ -15,6 +15,10 @@ the tiles add ~2^-15 relative at the sizes here.  The bound takes twice the
 two bf16 terms.  lse = m + ln(sum of the rounded weights): within 2^-9 of
 the exact log-sum-exp from the rounding, plus the score term; the bound is
 |lse - lse_ref| <= 2^-16 scale |q| max|k| + 2^-8 + 2^-14 |lse_ref|.
+With key splits each split's weights are rounded relative to its own
+maximum (the same 2^-9 per weight), and the merge scales a split's fp32
+numerator and normaliser by the same factor 2^(m_s - M): a few 2^-24
+relative more, inside the same bound.
 """
 from concurrent.futures import ThreadPoolExecutor
 
@@ -48,35 +52,43 @@ def queries(seed, n, H, d):
     return qb.reshape(n, H, d), f32_of_bits(qb).reshape(n, H, d)
 
 
-def check(nv, orc, ring, chunks, cfg, t, shot, qbits, qf, rows=None, scale=None):
+def check(nv, orc, ring, chunks, cfg, t, shot, qbits, qf, rows=None, scale=None,
+          key_splits=(0,)):
+    """Each split count in `key_splits` (0 = the library's choice) against
+    one oracle result."""
     Tc, H, d = cfg.chunk_tokens, cfg.heads, cfg.head_dim
     g_tok = cfg.sink_frames_global * cfg.tokens_per_frame
     s_tok = cfg.sink_frames_shot * cfg.tokens_per_frame
     scale = d ** -0.5 if scale is None else scale
     nq = qf.shape[0]
-    lse = torch.empty((nq, H), dtype=torch.float32, device="cuda")
-    o = ring.attention(t, bf16_gpu(qbits, (nq, H, d)), scale, lse=lse)
+    q = bf16_gpu(qbits, (nq, H, d))
+    runs = []
+    for ks in key_splits:
+        lse = torch.empty((nq, H), dtype=torch.float32, device="cuda")
+        runs.append((ks, ring.attention(t, q, scale, lse=lse, key_splits=ks), lse))
     _, Kr, Vr = orc.gather_window(chunks, t, Tc, cfg.window_chunks, g_tok, shot * Tc, s_tok)
     k = f32_of_bits(Kr).reshape(-1, H, d)
     v = f32_of_bits(Vr).reshape(-1, H, d)
     o_ref, a_ref, lse_ref = orc.attention_ref(qf, k, v, scale, rows=rows)
     torch.cuda.synchronize()
     sel = slice(None) if rows is None else torch.from_numpy(np.asarray(rows)).cuda()
-    og = o[sel].float().cpu().numpy().astype(np.float64)
-    lg = lse[sel].cpu().numpy().astype(np.float64)
-    if k.shape[0] == 0:
-        assert np.all(og == 0) and np.all(np.isneginf(lg)), f"step {t}: empty set"
-        return
-    qsel = qf if rows is None else qf[rows]
-    qn = np.linalg.norm(qsel.astype(np.float64), axis=2)                  # [n, H]
-    kmax = np.linalg.norm(k.astype(np.float64), axis=2).max(axis=0)        # [H]
-    sc = 2.0 ** -16 * scale * qn * kmax[None, :]
-    tol = 2.0 ** -8 * (a_ref + np.abs(o_ref)) + sc[..., None] * a_ref
-    err = np.abs(og - o_ref)
-    worst = np.unravel_index(np.argmax(err - tol), err.shape)
-    assert np.all(err <= tol), f"step {t}: o off at {worst}: {err[worst]} > {tol[worst]}"
-    ltol = sc + 2.0 ** -8 + 2.0 ** -14 * np.abs(lse_ref)
-    assert np.all(np.abs(lg - lse_ref) <= ltol), f"step {t}: lse off"
+    for ks, o, lse in runs:
+        og = o[sel].float().cpu().numpy().astype(np.float64)
+        lg = lse[sel].cpu().numpy().astype(np.float64)
+        if k.shape[0] == 0:
+            assert np.all(og == 0) and np.all(np.isneginf(lg)), f"step {t} splits {ks}: empty set"
+            continue
+        qsel = qf if rows is None else qf[rows]
+        qn = np.linalg.norm(qsel.astype(np.float64), axis=2)                  # [n, H]
+        kmax = np.linalg.norm(k.astype(np.float64), axis=2).max(axis=0)        # [H]
+        sc = 2.0 ** -16 * scale * qn * kmax[None, :]
+        tol = 2.0 ** -8 * (a_ref + np.abs(o_ref)) + sc[..., None] * a_ref
+        err = np.abs(og - o_ref)
+        worst = np.unravel_index(np.argmax(err - tol), err.shape)
+        assert np.all(err <= tol), \
+            f"step {t} splits {ks}: o off at {worst}: {err[worst]} > {tol[worst]}"
+        ltol = sc + 2.0 ** -8 + 2.0 ** -14 * np.abs(lse_ref)
+        assert np.all(np.abs(lg - lse_ref) <= ltol), f"step {t} splits {ks}: lse off"
 
 
 def small_cfg(nv, **kw):
@@ -104,13 +116,14 @@ def drive(nv, orc, cfg, cuts, steps, seed, at_step):
 def test_attention_every_step_small_ring(nv, orc):
     """Tc = 64, 2 heads, W = 2, a 16-token global sink and a 32-token shot
     sink, shot cuts at 0 and 4: empty set, sink-only, partial 64-key tiles,
-    up to four segments; 100 queries (a ragged query tile)."""
+    up to four segments; 100 queries (a ragged query tile).  One split, and
+    3 and 8 key splits (splits without tiles at the early steps)."""
     cfg = small_cfg(nv)
     qbits, qf = queries(3001, 100, cfg.heads, cfg.head_dim)
 
     def at(ring, chunks, t, shot):
         print("case: attention small ring step", t, flush=True)
-        check(nv, orc, ring, chunks, cfg, t, shot, qbits, qf)
+        check(nv, orc, ring, chunks, cfg, t, shot, qbits, qf, key_splits=(1, 3, 8))
 
     drive(nv, orc, cfg, {0, 4}, 8, 3002, at)
 
@@ -123,7 +136,7 @@ def test_attention_query_counts(nv, orc, nq):
     def at(ring, chunks, t, shot):
         if t == 5:
             print("case: attention nq", nq, flush=True)
-            check(nv, orc, ring, chunks, cfg, t, shot, qbits, qf)
+            check(nv, orc, ring, chunks, cfg, t, shot, qbits, qf, key_splits=(1, 2, 5))
 
     drive(nv, orc, cfg, {0, 3}, 6, 3004, at)
 
@@ -138,7 +151,7 @@ def test_attention_softmax_scales(nv, orc, scale):
     def at(ring, chunks, t, shot):
         if t == 7:  # global sink, shot sink (chunk 4, below the window), chunks 5 and 6
             print("case: attention scale", scale, flush=True)
-            check(nv, orc, ring, chunks, cfg, t, shot, qbits, qf, scale=scale)
+            check(nv, orc, ring, chunks, cfg, t, shot, qbits, qf, scale=scale, key_splits=(1, 4))
 
     drive(nv, orc, cfg, {0, 4}, 8, 3008, at)
 
@@ -147,8 +160,8 @@ def test_attention_64s_ring_step_15_sampled(nv, orc):
     """The 64 s ring (7040 tokens x 24 heads x 128 a chunk, W = 4, 3-frame
     sinks, shots at 0 and 10) at step 15: 7040 queries over the 33,440-token
     set (2640 + 2640 sink tokens and 4 window chunks), the launch the bench
-    times; 12 sampled queries (first and last included) x 24 heads against
-    the oracle."""
+    times (the library's split choice), and one split; 12 sampled queries
+    (first and last included) x 24 heads against the oracle."""
     print("case: attention 64 s ring step 15", flush=True)
     cfg = nv.KVConfig()
     Tc, H, d = cfg.chunk_tokens, cfg.heads, cfg.head_dim
@@ -174,11 +187,14 @@ def test_attention_64s_ring_step_15_sampled(nv, orc):
     qbits, qf = queries(3006, Tc, H, d)
     rows = np.unique(np.concatenate([[0, 127, 128, Tc - 1],
                                      np.random.default_rng(7).integers(0, Tc, 8)]))
-    check(nv, orc, ring, chunks, cfg, 15, 10, qbits, qf, rows=rows)
+    print("case: attention 64 s ring step 15 plan", ring.attention_plan(15, Tc), flush=True)
+    check(nv, orc, ring, chunks, cfg, 15, 10, qbits, qf, rows=rows, key_splits=(0, 1))
 
 
-def test_attention_deterministic(nv, orc):
-    """Fixed tile order and fixed in-tile order: two calls agree bit for bit."""
+@pytest.mark.parametrize("key_splits", [1, 3])
+def test_attention_deterministic(nv, orc, key_splits):
+    """Fixed tile order, fixed in-tile order and a fixed merge order: two
+    calls agree bit for bit."""
     cfg = small_cfg(nv)
     qbits, _ = queries(3009, 300, cfg.heads, cfg.head_dim)
 
@@ -187,8 +203,8 @@ def test_attention_deterministic(nv, orc):
             q = bf16_gpu(qbits, (300, cfg.heads, cfg.head_dim))
             l1 = torch.empty((300, cfg.heads), dtype=torch.float32, device="cuda")
             l2 = torch.empty_like(l1)
-            o1 = ring.attention(t, q, lse=l1)
-            o2 = ring.attention(t, q, lse=l2)
+            o1 = ring.attention(t, q, lse=l1, key_splits=key_splits)
+            o2 = ring.attention(t, q, lse=l2, key_splits=key_splits)
             torch.cuda.synchronize()
             assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
@@ -207,6 +223,11 @@ def test_attention_validation(nv):
         ring.attention(0, q, out=torch.empty((3, 2, 128), dtype=torch.bfloat16, device="cuda"))
     with pytest.raises(ValueError):
         ring.attention(0, q, lse=torch.empty((4, 3), dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError):
+        ring.attention(0, q, key_splits=2,
+                       workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    with pytest.raises(RuntimeError):
+        ring.attention(0, q, key_splits=9)
     ring64 = nv.KVRing(small_cfg(nv, head_dim=64))
     with pytest.raises(RuntimeError):
         ring64.attention(0, torch.zeros((4, 2, 64), dtype=torch.bfloat16, device="cuda"))
