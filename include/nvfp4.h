@@ -370,7 +370,7 @@ int nvfp4_gather_window(const nvfp4_kv_ring *ring, int64_t step, void *K_out, vo
  *     NVFP4_ATTN_MAX_SPLITS fixes the count (else NVFP4_EINVAL).  With s > 1
  *     splits the key set's 64-key tiles are cut into s consecutive runs of
  *     near-equal length, each run's partial softmax (fp32 unnormalised output,
- *     running maximum and sum of weights) goes to the workspace, and a second
+ *     reference maximum and sum of weights) goes to the workspace, and a second
  *     kernel combines the runs in index order, rescaling each by 2^(m_s - M)
  *     (the blockwise softmax merge).  Results depend on s only through fp32
  *     rounding and are identical from call to call for the same s.

@@ -18,7 +18,7 @@
 // SIMD, so one wave's softmax and dequantization run under the other's
 // MFMAs).  The effective set is walked segment by segment (each segment one
 // region: one key mean, one pair of decode scales), 64 keys a tile, through
-// two LDS stages.  Every tile is dequantized once per workgroup straight
+// three LDS stages.  Every tile is dequantized once per workgroup straight
 // from the packed ring (every lane one K block and half a V block for a
 // pair of keys) into
 //   K tile   [64 keys][128 d] bf16: 16-byte column c of key k in slot c ^ (k & 15)
@@ -28,16 +28,20 @@
 // the 64 banks.  Per tile and wave: S^T = K_hat Q^T on
 // v_mfma_f32_32x32x16_bf16 (a lane holds one query and 32 of the tile's
 // scores), the online softmax in registers (exp2 of the scores times
-// scale * log2 e), P^T rounded to bf16, O^T += V_hat^T P^T; the normaliser
-// sums the same bf16 weights (v_dot2_f32_bf16 against ones, two a step).  A lane of the
+// scale * log2 e, against a reference maximum that moves only when a score
+// passes it by more than 2^8), P^T rounded to bf16, O^T += V_hat^T P^T; the
+// normaliser sums the same bf16 weights (v_dot2_f32_bf16 against ones, two
+// a step).  A lane of the
 // 32x32 accumulator holds, for key block kb and element e, key
 // kb * 32 + h * 4 + (e >> 2) * 8 + (e & 3) (h = lane >> 5); V^T keeps key k of
 // each 16-key group at column ((k >> 2) & 1) * 8 + ((k >> 3) & 1) * 4 + (k & 3),
 // so the 8 keys of a lane's P^T operand slots are 16 contiguous bytes of V^T.
-// Each wave keeps its 32 queries in registers.  The packed blocks of tile
-// j + 2 are loaded during tile j, and tile j + 1 is dequantized into the
-// other stage in the same instruction stream as tile j's value MFMAs; one
-// barrier per tile.
+// Each wave keeps its 32 queries in registers.  Software pipeline, one
+// barrier per tile: during tile j the packed blocks of tile j + 3 are
+// loaded, tile j + 1's score MFMAs run among tile j's exponentials, and tile
+// j + 2 is dequantized into the third stage among tile j's value MFMAs.
+// With key splits, workgroup (split, query block, head) walks its split's
+// run of tiles and a merge kernel combines the runs.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -50,7 +54,7 @@ constexpr int kAQ = 256;                   // queries per workgroup (8 waves)
 constexpr int kAK = 64;                    // keys per tile
 constexpr int kATile = kAK * kAD * 2;      // bytes of the K tile (and of V^T)
 constexpr int kAStage = 2 * kATile;        // K tile, then V^T tile
-constexpr int kALds = 2 * kAStage;         // 64 KB
+constexpr int kALds = 3 * kAStage;         // 96 KB: three stages
 
 // Column of V^T that holds key k of a tile.
 __device__ __forceinline__ int vt_col(int k) {
@@ -161,6 +165,34 @@ __device__ __forceinline__ float half_sum(float v) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// S^T = K_hat Q^T for the K tile of stage `st`: two 32-key blocks,
+// alternating so that no MFMA waits for the one before it; fragment reads
+// four MFMAs ahead of their use.
+__device__ __forceinline__ void scores(const uint8_t *st, const bf16x8 (&qf)[8], int c, int h,
+                                       f32x16 (&sacc)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.0f;
+    constexpr int PF = 4;
+    bf16x8 kf[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+        const int ks = i >> 1, kb = i & 1;
+        kf[i] = *(const bf16x8 *)(st + (kb * 32 + c) * 256 + (((2 * ks + h) ^ (c & 15)) * 16));
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int ks = i >> 1, kb = i & 1;
+        const bf16x8 cur = kf[i % PF];
+        if (i + PF < 16) {
+            const int ks2 = (i + PF) >> 1, kb2 = (i + PF) & 1;
+            kf[i % PF] = *(const bf16x8 *)(st + (kb2 * 32 + c) * 256 + (((2 * ks2 + h) ^ (c & 15)) * 16));
+        }
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[ks], sacc[kb], 0, 0, 0);
+    }
+}
+
 __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     // workgroups of one (split, head) run on one XCD (b % 8), sharing its L2
@@ -197,64 +229,54 @@ __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
         for (int e = 0; e < 16; ++e) o[db][e] = 0.0f;
     float m_run = -__builtin_inff(), l_run = 0.0f;
 
-    // The split's tiles [jb, je).  Tile j + 1's blocks (tb, segment s_tb)
-    // were loaded one iteration earlier and are dequantized into the idle
-    // stage among tile j's value MFMAs; tile j + 2's are requested at the
-    // top of iteration j.  Past the last tile the loads repeat it and the
-    // extra stage write is never read, so the loop has no branch around them.
+    // The split's tiles [jb, je), three LDS stages: during iteration j the
+    // value MFMAs read tile j's stage, the score MFMAs of tile j + 1 (issued
+    // among tile j's exponentials) read the next, and tile j + 2's blocks,
+    // loaded one iteration earlier, are dequantized into the third among
+    // the value MFMAs; tile j + 3's are requested at the top.  Past the last
+    // tile the loads repeat it and the extra stage writes and scores are
+    // never used, so the loop has no branch around them.
     const int ntile = a.tile0[a.nseg];
     const int jb = (int)((int64_t)split * ntile / a.nsplit);
     const int je = (int)((int64_t)(split + 1) * ntile / a.nsplit);
+    uint8_t *s_cur = lds, *s_nxt = lds + kAStage, *s_fut = lds + 2 * kAStage;
     TileBlocks tb, tn;
     int s_tb = 0;
     if (je > jb) {
-        const int s0 = seg_of(a, jb);
+        int s0 = seg_of(a, jb);
         load_blocks(a, a.seg[s0], (jb - a.tile0[s0]) * kAK, t, head, tb);
-        store_blocks(lds, a.seg[s0], t, head, tb);
+        store_blocks(s_cur, a.seg[s0], t, head, tb);
         const int j1 = jb + 1 < je ? jb + 1 : jb;
-        s_tb = seg_of(a, j1);
-        load_blocks(a, a.seg[s_tb], (j1 - a.tile0[s_tb]) * kAK, t, head, tb);
+        s0 = seg_of(a, j1);
+        load_blocks(a, a.seg[s0], (j1 - a.tile0[s0]) * kAK, t, head, tb);
+        store_blocks(s_nxt, a.seg[s0], t, head, tb);
+        const int j2 = jb + 2 < je ? jb + 2 : je - 1;
+        s_tb = seg_of(a, j2);
+        load_blocks(a, a.seg[s_tb], (j2 - a.tile0[s_tb]) * kAK, t, head, tb);
     }
     __syncthreads();
+    f32x16 sacc[2];
+    scores(s_cur, qf, c, h, sacc);
+    // A zero scale (every weight 1: the mean of the values) runs as scores
+    // of 0 at scale 1, so that a masked key's -inf is never multiplied by 0.
+    const bool zero_scale = a.scale_log2 == 0.0f;
+    const float scale_log2 = zero_scale ? 1.0f : a.scale_log2;
 
     for (int j = jb; j < je; ++j) {
         const int sj = seg_of(a, j);
-        const int j2 = j + 2 < je ? j + 2 : je - 1;
-        const int s2 = seg_of(a, j2);
-        load_blocks(a, a.seg[s2], (j2 - a.tile0[s2]) * kAK, t, head, tn);
+        const int j3 = j + 3 < je ? j + 3 : je - 1;
+        const int s3 = seg_of(a, j3);
+        load_blocks(a, a.seg[s3], (j3 - a.tile0[s3]) * kAK, t, head, tn);
 
-        const uint8_t *st = lds + ((j - jb) & 1) * kAStage;
-        // S^T = K_hat Q^T: two 32-key blocks, alternating so that no MFMA
-        // waits for the one before it
-        f32x16 sacc[2];
+        if (zero_scale) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.0f;
-        {
-            // fragment reads four MFMAs ahead of their use
-            constexpr int PF = 4;
-            bf16x8 kf[PF];
-#pragma unroll
-            for (int i = 0; i < PF; ++i) {
-                const int ks = i >> 1, kb = i & 1;
-                kf[i] = *(const bf16x8 *)(st + (kb * 32 + c) * 256 + (((2 * ks + h) ^ (c & 15)) * 16));
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int ks = i >> 1, kb = i & 1;
-                const bf16x8 cur = kf[i % PF];
-                if (i + PF < 16) {
-                    const int ks2 = (i + PF) >> 1, kb2 = (i + PF) & 1;
-                    kf[i % PF] = *(const bf16x8 *)(st + (kb2 * 32 + c) * 256 + (((2 * ks2 + h) ^ (c & 15)) * 16));
-                }
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[ks], sacc[kb], 0, 0, 0);
-            }
+                for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.0f;
         }
         // keys past the segment's end
         const int64_t nvalid = a.seg[sj].n - (int64_t)(j - a.tile0[sj]) * kAK;
-        const bool partial = nvalid < kAK;
-        if (partial) {
+        if (nvalid < kAK) {
             // key kb*32 + h*4 + (e>>2)*8 + (e&3) against nvalid, the lane's
             // part moved to the right so each compare takes a constant
             const int lim = (int)nvalid - h * 4;
@@ -264,13 +286,31 @@ __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
                 for (int e = 0; e < 16; ++e)
                     if (kb * 32 + (e >> 2) * 8 + (e & 3) >= lim) sacc[kb][e] = -__builtin_inff();
         }
-        // online softmax
+        // online softmax against a reference maximum m_run (scale_log2 > 0,
+        // so a masked key's -inf stays -inf and its weight is exactly 0).
+        // The output and the normaliser are rescaled only when a tile's
+        // maximum exceeds the reference by more than 8 (log2 units) in some
+        // lane; in between the weights 2^(x - m_run) stay below 2^8, where
+        // bf16 and the fp32 sums keep the same relative rounding.
         float mx = sacc[0][0];
 #pragma unroll
         for (int e = 1; e < 32; ++e) mx = fmaxf(mx, sacc[e >> 4][e & 15]);
-        mx = half_max(mx);
-        const float m_new = fmaxf(m_run, mx * a.scale_log2);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        mx = half_max(mx) * scale_log2;
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.0f)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+            l_run *= alpha;
+            m_run = m_new;
+        }
+        // From here to the barrier one basic block: tile j + 1's score MFMAs
+        // among the exponentials, the value MFMAs among tile j + 2's
+        // dequantization.
+        f32x16 snx[2];
+        scores(s_nxt, qf, c, h, snx);
         float ps = 0.0f;
         const bf16x2 ones2 = __builtin_bit_cast(bf16x2, 0x3F803F80u);
         u32x4 pw[4];  // P^T operands: bf16 pairs
@@ -278,28 +318,13 @@ __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int e = 0; e < 16; e += 2) {
-                float x0 = __builtin_fmaf(sacc[kb][e], a.scale_log2, -m_new);
-                float x1 = __builtin_fmaf(sacc[kb][e + 1], a.scale_log2, -m_new);
-                if (partial) {
-                    // a masked key at scale 0 gives -inf * 0 = NaN: maxNum
-                    // turns it back into -inf (weight 0)
-                    x0 = fmaxf(x0, -__builtin_inff());
-                    x1 = fmaxf(x1, -__builtin_inff());
-                }
-                const float p0 = __builtin_amdgcn_exp2f(x0);
-                const float p1 = __builtin_amdgcn_exp2f(x1);
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][e], scale_log2, -m_run));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][e + 1], scale_log2, -m_run));
                 const uint32_t w = pack_bf16x2(p0, p1);
                 pw[kb * 2 + (e >> 3)][(e & 7) >> 1] = w;
                 ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones2, ps, false);
             }
-        l_run = __builtin_fmaf(l_run, alpha, ps);
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
-        }
-        m_run = m_new;
+        l_run += ps;
         // O^T += V_hat^T P^T, the four d blocks in turn (independent MFMAs)
         {
             // fragment reads four MFMAs ahead of their use
@@ -308,7 +333,7 @@ __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
                 const int kk = i >> 2, db = i & 3;
                 const int d = db * 32 + c;
                 const int sw = ((d >> 1) & 7) ^ ((d >> 4) & 7);
-                return (const bf16x8 *)(st + kATile + d * 128 + (((2 * kk + h) ^ sw) * 16));
+                return (const bf16x8 *)(s_cur + kATile + d * 128 + (((2 * kk + h) ^ sw) * 16));
             };
             bf16x8 vf[PF];
 #pragma unroll
@@ -322,16 +347,23 @@ __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
                                                                 o[db], 0, 0, 0);
             }
         }
-        store_blocks(lds + ((j - jb + 1) & 1) * kAStage, a.seg[s_tb], t, head, tb);
+        store_blocks(s_fut, a.seg[s_tb], t, head, tb);
         tb = tn;
-        s_tb = s2;
+        s_tb = s3;
+        sacc[0] = snx[0];
+        sacc[1] = snx[1];
+        uint8_t *const s_old = s_cur;
+        s_cur = s_nxt;
+        s_nxt = s_fut;
+        s_fut = s_old;
         __syncthreads();
     }
 
     // both lane halves saw every score maximum, so m_run agrees; the sums add
     const float lt = half_sum(l_run);
     if (a.nsplit > 1) {
-        // the split's share: unnormalised output and (max, sum of weights)
+        // the split's share: output and sum of weights, both relative to the
+        // reference maximum m_run, and m_run itself
         if (qi < a.nq) {
             const int64_t r = ((int64_t)split * a.nq + qi) * a.heads + head;
             float *po = a.part_o + r * kAD;
@@ -364,7 +396,7 @@ __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
 }
 
 // Merge of the key splits: thread (query, head, 8 d).  With M the largest
-// split maximum and w_s = 2^(m_s - M), o = sum_s w_s o_s / sum_s w_s l_s and
+// of the splits' reference maxima and w_s = 2^(m_s - M), o = sum_s w_s o_s / sum_s w_s l_s and
 // lse = (M + log2 sum_s w_s l_s) ln 2, splits in index order; a split
 // without keys has m = -inf and l = 0, and no keys at all give o = 0 and
 // lse = -inf as in the single-split kernel.

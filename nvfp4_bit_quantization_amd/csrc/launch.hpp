@@ -114,7 +114,7 @@ struct AttnArgs {
     float scale_log2;                // softmax scale * log2(e)
     // Key splits: workgroup (split, query block, head) takes the split's
     // share of the tiles; with nsplit > 1 it writes its unnormalised output
-    // and (running max in log2 units, sum of weights) to the workspace and a
+    // and (reference max in log2 units, sum of weights) to the workspace and a
     // second kernel merges the splits into o and lse.
     int32_t nsplit;
     float *part_ml;                  // [nsplit][nq][heads] (m, l)
