@@ -23,7 +23,7 @@
 // pair of keys) into
 //   K tile   [64 keys][128 d] bf16: 16-byte column c of key k in slot c ^ (k & 15)
 //   V^T tile [128 d][64 keys] bf16: keys permuted (below); 16-byte slot s of
-//            row d in s ^ ((d >> 1) & 7) ^ ((d >> 4) & 7)
+//            row d in s ^ ((d >> 1) & 7) ^ ((d >> 3) & 3)
 // so each fragment read (16 lanes x 16 bytes) meets 16 different groups of
 // the 64 banks.  Per tile and wave: S^T = K_hat Q^T on
 // v_mfma_f32_32x32x16_bf16 (a lane holds one query and 32 of the tile's
@@ -54,7 +54,15 @@ constexpr int kAQ = 256;                   // queries per workgroup (8 waves)
 constexpr int kAK = 64;                    // keys per tile
 constexpr int kATile = kAK * kAD * 2;      // bytes of the K tile (and of V^T)
 constexpr int kAStage = 2 * kATile;        // K tile, then V^T tile
+constexpr int kAVt = 3 * kATile;           // V^T tiles after the three K tiles
 constexpr int kALds = 3 * kAStage;         // 96 KB: three stages
+
+// 16-byte slot permutation of V^T row d.  A fragment read (16 lanes: rows
+// d0 + c, c = 0..15, one slot each) meets 16 different bank groups, and it
+// depends on d only through d & 31, so the four 32-row blocks of a read
+// share their lane offsets; the dequant's 4-byte writes meet at most 4 lanes
+// a bank.
+__device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) & 7) ^ ((d >> 3) & 3); }
 
 // Column of V^T that holds key k of a tile.
 __device__ __forceinline__ int vt_col(int k) {
@@ -110,9 +118,10 @@ __device__ __forceinline__ void load_blocks(const AttnArgs &a, const AttnSeg &sg
     }
 }
 
-// Dequantize a lane's blocks into `stage`: a K row segment and V^T columns.
-__device__ __forceinline__ void store_blocks(uint8_t *stage, const AttnSeg &sg, int t, int head,
-                                             const TileBlocks &tb) {
+// Dequantize a lane's blocks into a stage: a K row segment into the K tile
+// `kst`, V^T columns into the V^T tile `vst`.
+__device__ __forceinline__ void store_blocks(uint8_t *kst, uint8_t *vst, const AttnSeg &sg, int t,
+                                             int head, const TileBlocks &tb) {
     {
         const int k = t >> 3, b = t & 7;
         Raw16F32 m;
@@ -132,8 +141,8 @@ __device__ __forceinline__ void store_blocks(uint8_t *stage, const AttnSeg &sg, 
                        pack_bf16x2(y0[4], y0[5]), pack_bf16x2(y0[6], y0[7])};
         const u32x4 hi{pack_bf16x2(y1[0], y1[1]), pack_bf16x2(y1[2], y1[3]),
                        pack_bf16x2(y1[4], y1[5]), pack_bf16x2(y1[6], y1[7])};
-        *(u32x4 *)(stage + k * 256 + (((2 * b) ^ (k & 15)) * 16)) = lo;
-        *(u32x4 *)(stage + k * 256 + (((2 * b + 1) ^ (k & 15)) * 16)) = hi;
+        *(u32x4 *)(kst + k * 256 + (((2 * b) ^ (k & 15)) * 16)) = lo;
+        *(u32x4 *)(kst + k * 256 + (((2 * b + 1) ^ (k & 15)) * 16)) = hi;
     }
     {
         const float sdv = sg.sd[1];
@@ -146,8 +155,8 @@ __device__ __forceinline__ void store_blocks(uint8_t *stage, const AttnSeg &sg, 
 #pragma unroll
         for (int dd = 0; dd < 8; ++dd) {
             const int d = hb * 8 + dd;
-            const int phys = slot ^ ((d >> 1) & 7) ^ ((d >> 4) & 7);
-            *(uint32_t *)(stage + kATile + d * 128 + phys * 16 + off) = pack_bf16x2(y[0][dd], y[1][dd]);
+            const int phys = slot ^ vt_swz(d);
+            *(uint32_t *)(vst + d * 128 + phys * 16 + off) = pack_bf16x2(y[0][dd], y[1][dd]);
         }
     }
 }
@@ -191,6 +200,110 @@ __device__ __forceinline__ void scores(const uint8_t *st, const bf16x8 (&qf)[8],
         }
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[ks], sacc[kb], 0, 0, 0);
     }
+}
+
+// One tile of the loop, the stages fixed at compile time (so every LDS
+// address is a loop-invariant lane offset plus an immediate): tile j's K
+// and V^T tiles in stage CUR, tile j + 1's in NXT, tile j + 2 is written to
+// FUT.  sacc holds tile j's scores on entry and tile j + 1's on return.
+template <int CUR>
+__device__ __forceinline__ void attn_tile(const AttnArgs &a, uint8_t *lds, int j, int je, int t,
+                                          int head, int c, int h, bool zero_scale, float scale_log2,
+                                          const bf16x8 (&qf)[8], f32x16 (&o)[4], float &m_run,
+                                          float &l_run, f32x16 (&sacc)[2], TileBlocks &tb,
+                                          int &s_tb) {
+    constexpr int NXT = (CUR + 1) % 3, FUT = (CUR + 2) % 3;
+    const int sj = seg_of(a, j);
+    const int j3 = j + 3 < je ? j + 3 : je - 1;
+    const int s3 = seg_of(a, j3);
+    TileBlocks tn;
+    load_blocks(a, a.seg[s3], (j3 - a.tile0[s3]) * kAK, t, head, tn);
+
+    if (zero_scale) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.0f;
+    }
+    // keys past the segment's end
+    const int64_t nvalid = a.seg[sj].n - (int64_t)(j - a.tile0[sj]) * kAK;
+    if (nvalid < kAK) {
+        // key kb*32 + h*4 + (e>>2)*8 + (e&3) against nvalid, the lane's
+        // part moved to the right so each compare takes a constant
+        const int lim = (int)nvalid - h * 4;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if (kb * 32 + (e >> 2) * 8 + (e & 3) >= lim) sacc[kb][e] = -__builtin_inff();
+    }
+    // online softmax against a reference maximum m_run (scale_log2 > 0,
+    // so a masked key's -inf stays -inf and its weight is exactly 0).
+    // The output and the normaliser are rescaled only when a tile's
+    // maximum exceeds the reference by more than 8 (log2 units) in some
+    // lane; in between the weights 2^(x - m_run) stay below 2^8, where
+    // bf16 and the fp32 sums keep the same relative rounding.
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int e = 1; e < 32; ++e) mx = fmaxf(mx, sacc[e >> 4][e & 15]);
+    mx = half_max(mx) * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.0f)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
+    }
+    // From here to the barrier one basic block: tile j + 1's score MFMAs
+    // among the exponentials, the value MFMAs among tile j + 2's
+    // dequantization.
+    f32x16 snx[2];
+    scores(lds + NXT * kATile, qf, c, h, snx);
+    float ps = 0.0f;
+    const bf16x2 ones2 = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+    u32x4 pw[4];  // P^T operands: bf16 pairs
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][e], scale_log2, -m_run));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][e + 1], scale_log2, -m_run));
+            const uint32_t w = pack_bf16x2(p0, p1);
+            pw[kb * 2 + (e >> 3)][(e & 7) >> 1] = w;
+            ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones2, ps, false);
+        }
+    l_run += ps;
+    // O^T += V_hat^T P^T, the four d blocks in turn (independent MFMAs)
+    {
+        // fragment reads four MFMAs ahead of their use
+        constexpr int PF = 4;
+        auto vaddr = [&](int i) {
+            const int kk = i >> 2, db = i & 3;
+            const int d = db * 32 + c;
+            const int sw = vt_swz(d);
+            return (const bf16x8 *)(lds + kAVt + CUR * kATile + d * 128 + (((2 * kk + h) ^ sw) * 16));
+        };
+        bf16x8 vf[PF];
+#pragma unroll
+        for (int i = 0; i < PF; ++i) vf[i] = *vaddr(i);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int kk = i >> 2, db = i & 3;
+            const bf16x8 cur = vf[i % PF];
+            if (i + PF < 16) vf[i % PF] = *vaddr(i + PF);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, __builtin_bit_cast(bf16x8, pw[kk]),
+                                                            o[db], 0, 0, 0);
+        }
+    }
+    store_blocks(lds + FUT * kATile, lds + kAVt + FUT * kATile, a.seg[s_tb], t, head, tb);
+    tb = tn;
+    s_tb = s3;
+    sacc[0] = snx[0];
+    sacc[1] = snx[1];
+    __syncthreads();
 }
 
 __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
@@ -239,124 +352,34 @@ __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
     const int ntile = a.tile0[a.nseg];
     const int jb = (int)((int64_t)split * ntile / a.nsplit);
     const int je = (int)((int64_t)(split + 1) * ntile / a.nsplit);
-    uint8_t *s_cur = lds, *s_nxt = lds + kAStage, *s_fut = lds + 2 * kAStage;
-    TileBlocks tb, tn;
+    TileBlocks tb;
     int s_tb = 0;
     if (je > jb) {
         int s0 = seg_of(a, jb);
         load_blocks(a, a.seg[s0], (jb - a.tile0[s0]) * kAK, t, head, tb);
-        store_blocks(s_cur, a.seg[s0], t, head, tb);
+        store_blocks(lds, lds + kAVt, a.seg[s0], t, head, tb);
         const int j1 = jb + 1 < je ? jb + 1 : jb;
         s0 = seg_of(a, j1);
         load_blocks(a, a.seg[s0], (j1 - a.tile0[s0]) * kAK, t, head, tb);
-        store_blocks(s_nxt, a.seg[s0], t, head, tb);
+        store_blocks(lds + kATile, lds + kAVt + kATile, a.seg[s0], t, head, tb);
         const int j2 = jb + 2 < je ? jb + 2 : je - 1;
         s_tb = seg_of(a, j2);
         load_blocks(a, a.seg[s_tb], (j2 - a.tile0[s_tb]) * kAK, t, head, tb);
     }
     __syncthreads();
     f32x16 sacc[2];
-    scores(s_cur, qf, c, h, sacc);
+    scores(lds, qf, c, h, sacc);
     // A zero scale (every weight 1: the mean of the values) runs as scores
     // of 0 at scale 1, so that a masked key's -inf is never multiplied by 0.
     const bool zero_scale = a.scale_log2 == 0.0f;
     const float scale_log2 = zero_scale ? 1.0f : a.scale_log2;
 
-    for (int j = jb; j < je; ++j) {
-        const int sj = seg_of(a, j);
-        const int j3 = j + 3 < je ? j + 3 : je - 1;
-        const int s3 = seg_of(a, j3);
-        load_blocks(a, a.seg[s3], (j3 - a.tile0[s3]) * kAK, t, head, tn);
-
-        if (zero_scale) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.0f;
-        }
-        // keys past the segment's end
-        const int64_t nvalid = a.seg[sj].n - (int64_t)(j - a.tile0[sj]) * kAK;
-        if (nvalid < kAK) {
-            // key kb*32 + h*4 + (e>>2)*8 + (e&3) against nvalid, the lane's
-            // part moved to the right so each compare takes a constant
-            const int lim = (int)nvalid - h * 4;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    if (kb * 32 + (e >> 2) * 8 + (e & 3) >= lim) sacc[kb][e] = -__builtin_inff();
-        }
-        // online softmax against a reference maximum m_run (scale_log2 > 0,
-        // so a masked key's -inf stays -inf and its weight is exactly 0).
-        // The output and the normaliser are rescaled only when a tile's
-        // maximum exceeds the reference by more than 8 (log2 units) in some
-        // lane; in between the weights 2^(x - m_run) stay below 2^8, where
-        // bf16 and the fp32 sums keep the same relative rounding.
-        float mx = sacc[0][0];
-#pragma unroll
-        for (int e = 1; e < 32; ++e) mx = fmaxf(mx, sacc[e >> 4][e & 15]);
-        mx = half_max(mx) * scale_log2;
-        if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.0f)) {
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
-            l_run *= alpha;
-            m_run = m_new;
-        }
-        // From here to the barrier one basic block: tile j + 1's score MFMAs
-        // among the exponentials, the value MFMAs among tile j + 2's
-        // dequantization.
-        f32x16 snx[2];
-        scores(s_nxt, qf, c, h, snx);
-        float ps = 0.0f;
-        const bf16x2 ones2 = __builtin_bit_cast(bf16x2, 0x3F803F80u);
-        u32x4 pw[4];  // P^T operands: bf16 pairs
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int e = 0; e < 16; e += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][e], scale_log2, -m_run));
-                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][e + 1], scale_log2, -m_run));
-                const uint32_t w = pack_bf16x2(p0, p1);
-                pw[kb * 2 + (e >> 3)][(e & 7) >> 1] = w;
-                ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones2, ps, false);
-            }
-        l_run += ps;
-        // O^T += V_hat^T P^T, the four d blocks in turn (independent MFMAs)
-        {
-            // fragment reads four MFMAs ahead of their use
-            constexpr int PF = 4;
-            auto vaddr = [&](int i) {
-                const int kk = i >> 2, db = i & 3;
-                const int d = db * 32 + c;
-                const int sw = ((d >> 1) & 7) ^ ((d >> 4) & 7);
-                return (const bf16x8 *)(s_cur + kATile + d * 128 + (((2 * kk + h) ^ sw) * 16));
-            };
-            bf16x8 vf[PF];
-#pragma unroll
-            for (int i = 0; i < PF; ++i) vf[i] = *vaddr(i);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int kk = i >> 2, db = i & 3;
-                const bf16x8 cur = vf[i % PF];
-                if (i + PF < 16) vf[i % PF] = *vaddr(i + PF);
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, __builtin_bit_cast(bf16x8, pw[kk]),
-                                                                o[db], 0, 0, 0);
-            }
-        }
-        store_blocks(s_fut, a.seg[s_tb], t, head, tb);
-        tb = tn;
-        s_tb = s3;
-        sacc[0] = snx[0];
-        sacc[1] = snx[1];
-        uint8_t *const s_old = s_cur;
-        s_cur = s_nxt;
-        s_nxt = s_fut;
-        s_fut = s_old;
-        __syncthreads();
+    for (int j = jb; j < je; j += 3) {
+        attn_tile<0>(a, lds, j, je, t, head, c, h, zero_scale, scale_log2, qf, o, m_run, l_run, sacc, tb, s_tb);
+        if (j + 1 >= je) break;
+        attn_tile<1>(a, lds, j + 1, je, t, head, c, h, zero_scale, scale_log2, qf, o, m_run, l_run, sacc, tb, s_tb);
+        if (j + 2 >= je) break;
+        attn_tile<2>(a, lds, j + 2, je, t, head, c, h, zero_scale, scale_log2, qf, o, m_run, l_run, sacc, tb, s_tb);
     }
 
     // both lane halves saw every score maximum, so m_run agrees; the sums add
