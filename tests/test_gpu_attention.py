@@ -231,3 +231,50 @@ def test_attention_validation(nv):
     ring64 = nv.KVRing(small_cfg(nv, head_dim=64))
     with pytest.raises(RuntimeError):
         ring64.attention(0, torch.zeros((4, 2, 64), dtype=torch.bfloat16, device="cuda"))
+
+
+def test_attention_auto_splits_follow_the_model(nv):
+    """The library's split choice equals the cost model its header states,
+    evaluated here with this device's compute-unit count: ceil(n s / CUs)
+    rounds of 1/s, times 1 + 0.015 s, the cheapest s in 1..8 taken if it
+    saves 3% over one split and every split keeps 8 tiles (white-box: the
+    ring's counters are set as stores and shot starts would set them)."""
+    import math
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def model(units, ntile):
+        if units == 0 or ntile < 16:
+            return 1
+        cost = lambda sp: math.ceil(units * sp / cus) / sp * (1.0 + 0.015 * sp)
+        best = 1
+        for sp in range(2, 9):
+            if ntile < 8 * sp:
+                break
+            if cost(sp) < cost(best):
+                best = sp
+        return best if cost(best) <= 0.97 * cost(1) else 1
+
+    cfg = nv.KVConfig()
+    ring = nv.KVRing(cfg)
+    Tc = cfg.chunk_tokens
+    g = cfg.sink_frames_global * cfg.tokens_per_frame
+    for step, shot in [(1, 0), (3, 0), (15, 10), (25, 20)]:
+        ring.ring.next_chunk = step
+        ring.ring.s_start = shot * Tc
+        # the segments: the global sink below the window, the shot sink's
+        # part above the global sink and below the window, the window chunks
+        win_lo = max(0, step - cfg.window_chunks) * Tc
+        n_g = min(g, win_lo)
+        s_hi = min(shot * Tc + cfg.sink_frames_shot * cfg.tokens_per_frame, win_lo)
+        n_s = max(0, s_hi - max(shot * Tc, n_g))
+        n_chunks = step - max(0, step - cfg.window_chunks)
+        assert n_g + n_s + n_chunks * Tc == ring.effective_tokens(step), step
+        ntile = -(-n_g // 64) + -(-n_s // 64) + n_chunks * -(-Tc // 64)
+        for nq in [0, 1, 256, 2048, 7040, 14080, 70400]:
+            sp, wsb = ring.attention_plan(step, nq)
+            units = -(-nq // 256) * cfg.heads
+            assert sp == model(units, ntile), (step, nq, sp, model(units, ntile))
+            rows = sp * nq * cfg.heads
+            assert wsb == (0 if sp == 1 else -(-rows * 8 // 256) * 256 + rows * 512)
+    print("case: auto splits on", cus, "CUs", flush=True)
