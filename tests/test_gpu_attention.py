@@ -194,7 +194,8 @@ def test_attention_64s_ring_step_15_sampled(nv, orc):
 @pytest.mark.parametrize("key_splits", [1, 3])
 def test_attention_deterministic(nv, orc, key_splits):
     """Fixed tile order, fixed in-tile order and a fixed merge order: two
-    calls agree bit for bit."""
+    calls agree bit for bit, and a third without the lse output gives the
+    same o."""
     cfg = small_cfg(nv)
     qbits, _ = queries(3009, 300, cfg.heads, cfg.head_dim)
 
@@ -205,8 +206,9 @@ def test_attention_deterministic(nv, orc, key_splits):
             l2 = torch.empty_like(l1)
             o1 = ring.attention(t, q, lse=l1, key_splits=key_splits)
             o2 = ring.attention(t, q, lse=l2, key_splits=key_splits)
+            o3 = ring.attention(t, q, key_splits=key_splits)  # no lse output
             torch.cuda.synchronize()
-            assert torch.equal(o1, o2) and torch.equal(l1, l2)
+            assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(o1, o3)
 
     drive(nv, orc, cfg, {0, 4}, 8, 3010, at)
 
