@@ -348,7 +348,8 @@ __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
     // loaded one iteration earlier, are dequantized into the third among
     // the value MFMAs; tile j + 3's are requested at the top.  Past the last
     // tile the loads repeat it and the extra stage writes and scores are
-    // never used, so the loop has no branch around them.
+    // never used, so a tile has no branch around them.  The loop is unrolled
+    // by the three stages (attn_tile<0..2>), tile jb in stage 0.
     const int ntile = a.tile0[a.nseg];
     const int jb = (int)((int64_t)split * ntile / a.nsplit);
     const int je = (int)((int64_t)(split + 1) * ntile / a.nsplit);
