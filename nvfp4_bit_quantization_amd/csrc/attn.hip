@@ -23,7 +23,7 @@
 // pair of keys) into
 //   K tile   [64 keys][128 d] bf16: 16-byte column c of key k in slot c ^ (k & 15)
 //   V^T tile [128 d][64 keys] bf16: keys permuted (below); 16-byte slot s of
-//            row d in s ^ ((d >> 1) & 7) ^ ((d >> 3) & 3)
+//            row d in s ^ ((d >> 1) & 7) ^ ((d >> 4) & 7)
 // so each fragment read (16 lanes x 16 bytes) meets 16 different groups of
 // the 64 banks.  Per tile and wave: S^T = K_hat Q^T on
 // v_mfma_f32_32x32x16_bf16 (a lane holds one query and 32 of the tile's
@@ -58,11 +58,13 @@ constexpr int kAVt = 3 * kATile;           // V^T tiles after the three K tiles
 constexpr int kALds = 3 * kAStage;         // 96 KB: three stages
 
 // 16-byte slot permutation of V^T row d.  A fragment read (16 lanes: rows
-// d0 + c, c = 0..15, one slot each) meets 16 different bank groups, and it
-// depends on d only through d & 31, so the four 32-row blocks of a read
-// share their lane offsets; the dequant's 4-byte writes meet at most 4 lanes
-// a bank.
-__device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) & 7) ^ ((d >> 3) & 3); }
+// d0 + c, c = 0..15, one slot each) meets 16 different bank groups, and the
+// dequant's 4-byte writes (16 rows 8 apart per 16 lanes) two lanes a bank.
+// For row d = 32 db + c it is vt_swz_lo(c) ^ 2 db, so slot 2 kk + h of
+// block db is slot 2 (kk ^ db) + h of block 0 moved by db rows of 32: the
+// reads of all four blocks share four lane offsets.
+__device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) & 7) ^ ((d >> 4) & 7); }
+__device__ __forceinline__ int vt_swz_lo(int c) { return ((c >> 1) & 7) ^ (c >> 4); }
 
 // Column of V^T that holds key k of a tile.
 __device__ __forceinline__ int vt_col(int k) {
@@ -282,9 +284,9 @@ __device__ __forceinline__ void attn_tile(const AttnArgs &a, uint8_t *lds, int j
         constexpr int PF = 4;
         auto vaddr = [&](int i) {
             const int kk = i >> 2, db = i & 3;
-            const int d = db * 32 + c;
-            const int sw = vt_swz(d);
-            return (const bf16x8 *)(lds + kAVt + CUR * kATile + d * 128 + (((2 * kk + h) ^ sw) * 16));
+            const int kx = kk ^ db;  // compile-time: the block-0 slot pair
+            return (const bf16x8 *)(lds + kAVt + CUR * kATile + db * 4096 + c * 128 +
+                                    (((2 * kx + h) ^ vt_swz_lo(c)) * 16));
         };
         bf16x8 vf[PF];
 #pragma unroll
