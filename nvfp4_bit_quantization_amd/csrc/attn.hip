@@ -213,11 +213,19 @@ __device__ __forceinline__ void attn_tile(const AttnArgs &a, uint8_t *lds, int j
                                           int head, int c, int h, bool zero_scale, float scale_log2,
                                           const bf16x8 (&qf)[8], f32x16 (&o)[4], float &m_run,
                                           float &l_run, f32x16 (&sacc)[2], TileBlocks &tb,
-                                          int &s_tb) {
+                                          int &s_tb, int &sj, int &sj_end, int &s3, int &s3_end) {
     constexpr int NXT = (CUR + 1) % 3, FUT = (CUR + 2) % 3;
-    const int sj = seg_of(a, j);
+    // segment cursors of tile j and of tile j + 3 (both move by at most one
+    // tile per tile, and every segment has a tile, so one step suffices)
+    if (j >= sj_end) {
+        ++sj;
+        sj_end = a.tile0[sj + 1];
+    }
     const int j3 = j + 3 < je ? j + 3 : je - 1;
-    const int s3 = seg_of(a, j3);
+    if (j3 >= s3_end) {
+        ++s3;
+        s3_end = a.tile0[s3 + 1];
+    }
     TileBlocks tn;
     load_blocks(a, a.seg[s3], (j3 - a.tile0[s3]) * kAK, t, head, tn);
 
@@ -357,6 +365,8 @@ __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
     const int je = (int)((int64_t)(split + 1) * ntile / a.nsplit);
     TileBlocks tb;
     int s_tb = 0;
+    int sj = seg_of(a, jb);
+    int sj_end = a.tile0[sj + 1];
     if (je > jb) {
         int s0 = seg_of(a, jb);
         load_blocks(a, a.seg[s0], (jb - a.tile0[s0]) * kAK, t, head, tb);
@@ -376,13 +386,15 @@ __global__ __launch_bounds__(512) void attn_window_kernel(AttnArgs a) {
     // of 0 at scale 1, so that a masked key's -inf is never multiplied by 0.
     const bool zero_scale = a.scale_log2 == 0.0f;
     const float scale_log2 = zero_scale ? 1.0f : a.scale_log2;
+    int s3 = s_tb;  // segment of tile min(jb + 2, je - 1)
+    int s3_end = a.tile0[s3 + 1];
 
     for (int j = jb; j < je; j += 3) {
-        attn_tile<0>(a, lds, j, je, t, head, c, h, zero_scale, scale_log2, qf, o, m_run, l_run, sacc, tb, s_tb);
+        attn_tile<0>(a, lds, j, je, t, head, c, h, zero_scale, scale_log2, qf, o, m_run, l_run, sacc, tb, s_tb, sj, sj_end, s3, s3_end);
         if (j + 1 >= je) break;
-        attn_tile<1>(a, lds, j + 1, je, t, head, c, h, zero_scale, scale_log2, qf, o, m_run, l_run, sacc, tb, s_tb);
+        attn_tile<1>(a, lds, j + 1, je, t, head, c, h, zero_scale, scale_log2, qf, o, m_run, l_run, sacc, tb, s_tb, sj, sj_end, s3, s3_end);
         if (j + 2 >= je) break;
-        attn_tile<2>(a, lds, j + 2, je, t, head, c, h, zero_scale, scale_log2, qf, o, m_run, l_run, sacc, tb, s_tb);
+        attn_tile<2>(a, lds, j + 2, je, t, head, c, h, zero_scale, scale_log2, qf, o, m_run, l_run, sacc, tb, s_tb, sj, sj_end, s3, s3_end);
     }
 
     // both lane halves saw every score maximum, so m_run agrees; the sums add
