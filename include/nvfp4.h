@@ -71,6 +71,10 @@ enum { NVFP4_SEARCH_6 = 0, NVFP4_SEARCH_4O6 = 1 };
 
 /* Library ABI version (NVFP4_ABI_VERSION of the built library). */
 int nvfp4_abi_version(void);
+/* Identity of the build: a digest of the sources the library was compiled
+ * from (static text).  The Python binding refuses a library whose digest
+ * differs from that of the sources next to it. */
+const char *nvfp4_build_hash(void);
 /* Static text for a status code. */
 const char *nvfp4_status_string(int status);
 /* Detail of the last failure on the calling thread ("" if none). */
@@ -316,10 +320,14 @@ int nvfp4_kv_begin_shot(nvfp4_kv_ring *ring, int64_t chunk_idx);
  * Quantize chunk `chunk_idx` (must equal ring->next_chunk) into its ring
  * slot (DeepRead summary: chunk-level KV quantization, keys K-smoothed).
  *   K, V: device bf16 [T_c, H, d].
- *   mu[h, c] = (float)(sum / T_c), the per-channel key sum taken in double
- *   in a fixed order: tiles of 16 tokens, each summed in token order, then
- *   the tile sums (zero padded to a power-of-two count) added pairwise level
- *   by level; K_s = RN(K - mu).  K_s and V are each quantized 1-D along (h, c) with one FP32
+ *   mu[h, c] = (float)RN64(S / T_c), S the exact sum of the chunk's T_c keys
+ *   of channel (h, c) (the exact quotient rounded to double, then to float);
+ *   K_s = RN(K - mu).  The kernels sum in double, which is exact, so mu is
+ *   exactly that, whenever sum_t |K[t, h, c]| < 2^53 * 2^k with 2^k the
+ *   largest power of two dividing every nonzero key of the channel (for
+ *   bf16 keys it suffices that their exponents span at most 45 - log2(T_c)
+ *   binades: 32 at T_c = 7040); outside that domain mu may differ from it
+ *   in the last bit.  K_s and V are each quantized 1-D along (h, c) with one FP32
  *   tensor scale per chunk.  Chunk 0 also fills the global-sink region and
  *   the first chunk of a shot fills the shot-sink region (byte copies of the
  *   leading sink tokens, written by the same kernel).  Advances next_chunk.

@@ -62,6 +62,7 @@ _lib = None
 
 _EXPORTS = {
     "nvfp4_abi_version": ([], C.c_int),
+    "nvfp4_build_hash": ([], C.c_char_p),
     "nvfp4_status_string": ([C.c_int], C.c_char_p),
     "nvfp4_last_error": ([], C.c_char_p),
     "nvfp4_codes_bytes": ([C.c_int64, C.c_int64], C.c_size_t),
@@ -107,13 +108,22 @@ _EXPORTS = {
 
 
 def lib():
-    """The loaded libnvfp4.so (raises if it has not been built)."""
+    """The loaded libnvfp4.so (raises if it has not been built, or was built
+    from other sources than the ones beside it)."""
     global _lib
     if _lib is None:
+        from . import build as _build
+
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built: run python -m "
                                "nvfp4_bit_quantization_amd.build")
         L = C.CDLL(LIB_PATH)
+        L.nvfp4_build_hash.restype = C.c_char_p
+        built, now = L.nvfp4_build_hash().decode(), _build.source_hash()
+        if built != now:
+            raise RuntimeError(f"{LIB_PATH} was built from other sources (digest {built}, "
+                               f"sources {now}): rebuild with python -m "
+                               "nvfp4_bit_quantization_amd.build")
         for name, (args, res) in _EXPORTS.items():
             fn = getattr(L, name)
             fn.argtypes = args

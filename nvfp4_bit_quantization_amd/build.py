@@ -8,6 +8,7 @@ packed-fp32 instructions disabled.
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import subprocess
 import sys
@@ -33,9 +34,24 @@ COMMON = [
 ]
 
 
-def _compile(src: str) -> str:
+def source_hash() -> str:
+    """sha256 (first 16 hex digits) of every source, header and build flag the
+    library is made from; compiled into the library (nvfp4_build_hash) so
+    that a library older than its sources is refused at load time."""
+    h = hashlib.sha256()
+    for f in SOURCES + HEADERS:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    with open(os.path.join(ROOT, "include", "nvfp4.h"), "rb") as fh:
+        h.update(fh.read())
+    h.update(" ".join(c for c in COMMON if not c.startswith("-I")).encode())  # no paths
+    return h.hexdigest()[:16]
+
+
+def _compile(src: str, digest: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, f'-DNVFP4_BUILD_HASH="{digest}"', "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l
                     and "not a recognized feature" not in l)
@@ -48,8 +64,9 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
+    digest = source_hash()
     with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(lambda src: _compile(src, digest), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
@@ -60,12 +77,18 @@ def build(verbose: bool = False) -> str:
 
 
 def stale() -> bool:
+    """True if the library is missing or was built from other sources (by
+    content, not file times, which a copy of the tree may not keep)."""
     if not os.path.exists(LIB):
         return True
-    t = os.path.getmtime(LIB)
-    files = [os.path.join(CSRC, f) for f in SOURCES + HEADERS]
-    files.append(os.path.join(ROOT, "include", "nvfp4.h"))
-    return any(os.path.getmtime(f) > t for f in files)
+    import ctypes
+
+    try:
+        fn = ctypes.CDLL(LIB).nvfp4_build_hash
+    except (OSError, AttributeError):
+        return True
+    fn.restype = ctypes.c_char_p
+    return fn().decode() != source_hash()
 
 
 if __name__ == "__main__":

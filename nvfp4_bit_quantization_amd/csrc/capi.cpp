@@ -152,6 +152,11 @@ extern "C" {
 
 int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
 
+#ifndef NVFP4_BUILD_HASH
+#define NVFP4_BUILD_HASH "unknown"
+#endif
+const char *nvfp4_build_hash(void) { return NVFP4_BUILD_HASH; }
+
 const char *nvfp4_status_string(int status) {
     switch (status) {
     case NVFP4_OK: return "ok";

@@ -214,24 +214,79 @@ def kv_mean(K) -> np.ndarray:
     return mu
 
 
-def kv_encode_chunk(K, V, search: int = SEARCH_4O6) -> dict:
-    """K, V float32 [T, HD] (bf16 values) -> packed chunk dict."""
+def kv_encode_chunk(K, V, search: int = SEARCH_4O6, threads: int = 1, rows=None) -> dict:
+    """K, V float32 [T, HD] (bf16 values) -> packed chunk dict.
+
+    threads == 1 and rows is None: one call of the C routine
+    orc_kv_encode_chunk.  Otherwise the same encoding assembled from the C
+    routines by a driver: the key mean over the whole chunk (orc_kv_mean),
+    K_s = RN(K - mu) (one float32 subtraction per element), the tensor amax
+    of K_s and of V over the whole chunk, then orc_quantize with that amax on
+    contiguous row ranges, `threads` of them at once (ctypes releases the GIL
+    during each C call; the blocks of a row depend only on the row and the
+    tensor scale, so the split changes nothing).  With `rows` (token indices)
+    only those tokens are encoded (the statistics still cover every token):
+    the arrays then hold those rows, in the order given.
+    """
     K = _f32(K)
     V = _f32(V)
     T, HD = K.shape
-    kc = np.zeros((T, HD // 2), np.uint8)
-    ks = np.zeros((T, HD // 16), np.uint8)
-    vc = np.zeros((T, HD // 2), np.uint8)
-    vs = np.zeros((T, HD // 16), np.uint8)
-    mu = np.zeros(HD, np.float32)
-    sdk, sdv = C.c_float(), C.c_float()
-    rc = lib().orc_kv_encode_chunk(K.reshape(-1), V.reshape(-1), T, HD, search, kc.reshape(-1),
-                                   ks.reshape(-1), C.byref(sdk), vc.reshape(-1), vs.reshape(-1),
-                                   C.byref(sdv), mu)
-    if rc != 0:
-        raise RuntimeError("orc_kv_encode_chunk failed")
-    return dict(kc=kc, ks=ks, sdk=np.float32(sdk.value), vc=vc, vs=vs,
-                sdv=np.float32(sdv.value), mu=mu)
+    if threads <= 1 and rows is None:
+        kc = np.zeros((T, HD // 2), np.uint8)
+        ks = np.zeros((T, HD // 16), np.uint8)
+        vc = np.zeros((T, HD // 2), np.uint8)
+        vs = np.zeros((T, HD // 16), np.uint8)
+        mu = np.zeros(HD, np.float32)
+        sdk, sdv = C.c_float(), C.c_float()
+        rc = lib().orc_kv_encode_chunk(K.reshape(-1), V.reshape(-1), T, HD, search,
+                                       kc.reshape(-1), ks.reshape(-1), C.byref(sdk),
+                                       vc.reshape(-1), vs.reshape(-1), C.byref(sdv), mu)
+        if rc != 0:
+            raise RuntimeError("orc_kv_encode_chunk failed")
+        return dict(kc=kc, ks=ks, sdk=np.float32(sdk.value), vc=vc, vs=vs,
+                    sdv=np.float32(sdv.value), mu=mu)
+    mu = kv_mean(K)
+    Ks = K - mu[None, :]
+    ak, av = amax(Ks), amax(V)
+    if rows is not None:
+        rows = np.asarray(rows, np.int64)
+        Ks, V = np.ascontiguousarray(Ks[rows]), np.ascontiguousarray(V[rows])
+    n = Ks.shape[0]
+    parts = max(1, min(threads, n // 16)) if n else 1
+    cuts = [n * i // parts for i in range(parts + 1)]
+
+    def enc(i):
+        a, b = cuts[i], cuts[i + 1]
+        return quantize(Ks[a:b], search=search, amax=ak), quantize(V[a:b], search=search, amax=av)
+
+    if parts > 1:
+        from concurrent.futures import ThreadPoolExecutor
+
+        with ThreadPoolExecutor(parts) as ex:
+            out = list(ex.map(enc, range(parts)))
+    else:
+        out = [enc(0)]
+    cat = lambda j, which: np.concatenate([o[which][j] for o in out]) if n else \
+        np.zeros((0, HD // (2 if j == 0 else 16)), np.uint8)
+    sdk = tensor_scales(ak)[1]
+    sdv = tensor_scales(av)[1]
+    return dict(kc=cat(0, 0), ks=cat(1, 0), sdk=sdk, vc=cat(0, 1), vs=cat(1, 1), sdv=sdv, mu=mu)
+
+
+def kv_dequant_rows(chunk: dict, key: bool, threads: int = 1) -> np.ndarray:
+    """bf16 bits of every row of an encoded chunk (the whole chunk, or the
+    rows it was encoded for), `threads` row ranges at once."""
+    n = chunk["kc"].shape[0]
+    parts = max(1, min(threads, n // 16)) if n else 1
+    cuts = [n * i // parts for i in range(parts + 1)]
+    if parts == 1:
+        return kv_dequant_tokens(chunk, 0, n, key)
+    from concurrent.futures import ThreadPoolExecutor
+
+    with ThreadPoolExecutor(parts) as ex:
+        out = list(ex.map(lambda i: kv_dequant_tokens(chunk, cuts[i], cuts[i + 1] - cuts[i], key),
+                          range(parts)))
+    return np.concatenate(out)
 
 
 def kv_dequant_tokens(chunk: dict, tok0: int, ntok: int, key: bool) -> np.ndarray:

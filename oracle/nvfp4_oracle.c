@@ -311,34 +311,125 @@ void orc_to_bf16(const float *x, int64_t n, uint16_t *out)
 /* KV cache: K-smoothing and chunk encoding                            */
 /* ------------------------------------------------------------------ */
 
+/* Exact sum of float values.  Every finite float is M * 2^(P - 149) with
+ * an integer 0 <= M < 2^24 and 0 <= P <= 253, so a sum of floats is an
+ * integer multiple of 2^-149.  The accumulator holds that integer as
+ * KM_DIGITS signed base-2^32 digits, d[0] the least significant, with the
+ * carries left unpropagated until the end (each digit stays below 2^63 for
+ * fewer than 2^31 terms); the most significant bit a float can set is bit
+ * 253 + 24, so 12 digits (384 bits) leave room for the carries of 2^31
+ * terms.  No step rounds. */
+#define KM_DIGITS 12
+
+static void exact_add(int64_t *d, float v)
+{
+    uint32_t u;
+    memcpy(&u, &v, 4);
+    uint32_t be = (u >> 23) & 0xFFu, frac = u & 0x7FFFFFu;
+    uint64_t M = be ? (uint64_t)(frac | 0x800000u) : (uint64_t)frac;
+    int P = be ? (int)be - 1 : 0; /* normal: 1.f * 2^(be-127) = M * 2^(be-150) */
+    if (M == 0)
+        return;
+    uint64_t w = M << (P % 32); /* < 2^56 */
+    int64_t lo = (int64_t)(w & 0xFFFFFFFFu), hi = (int64_t)(w >> 32);
+    if (u >> 31) {
+        lo = -lo;
+        hi = -hi;
+    }
+    d[P / 32] += lo;
+    d[P / 32 + 1] += hi;
+}
+
+/* Sign (+1, -1 or 0) and magnitude (base-2^32 digits) of the accumulated
+ * integer: carries propagated in two's complement, a negative result
+ * negated. */
+static int exact_magnitude(const int64_t *d, uint32_t *mag)
+{
+    int64_t carry = 0;
+    for (int i = 0; i < KM_DIGITS; ++i) {
+        int64_t x = d[i] + carry;
+        int64_t low = x & 0xFFFFFFFF;
+        mag[i] = (uint32_t)low;
+        carry = (x - low) / 4294967296LL;
+    }
+    int sign = carry < 0 ? -1 : 1;
+    if (sign < 0) { /* two's complement negation of the digit string */
+        uint64_t c = 1;
+        for (int i = 0; i < KM_DIGITS; ++i) {
+            uint64_t x = (uint64_t)(uint32_t)~mag[i] + c;
+            mag[i] = (uint32_t)x;
+            c = x >> 32;
+        }
+    }
+    int nz = 0;
+    for (int i = 0; i < KM_DIGITS; ++i)
+        nz |= mag[i] != 0;
+    return nz ? sign : 0;
+}
+
+/* RN64(N * 2^-149 / T) for the integer N given by sign and magnitude, T >= 1:
+ * the long division of N * 2^96 by T (base 2^32, exact quotient Q and
+ * remainder), then Q rounded to 53 significant bits, ties to even, with the
+ * bits below the guard bit and the remainder as the sticky bit.  N >= 1 and
+ * T < 2^31 make Q >= 2^65, so 53 bits, the guard bit and the sticky bit are
+ * all there; the result is a normal double (>= 2^-180). */
+static double exact_quotient(int sign, const uint32_t *mag, uint32_t T)
+{
+    enum { ND = KM_DIGITS + 3 };
+    uint32_t num[ND], quo[ND];
+    if (sign == 0)
+        return 0.0;
+    for (int i = 0; i < 3; ++i)
+        num[i] = 0;
+    for (int i = 0; i < KM_DIGITS; ++i)
+        num[i + 3] = mag[i];
+    uint64_t rem = 0;
+    for (int i = ND - 1; i >= 0; --i) {
+        uint64_t cur = (rem << 32) | num[i];
+        quo[i] = (uint32_t)(cur / T);
+        rem = cur % T;
+    }
+#define QBIT(b) ((quo[(b) / 32] >> ((b) % 32)) & 1u)
+    int p = ND * 32 - 1;
+    while (!QBIT(p))
+        --p;
+    uint64_t mant = 0;
+    for (int b = p; b > p - 53; --b)
+        mant = 2 * mant + QBIT(b);
+    int guard = (int)QBIT(p - 53);
+    int sticky = rem != 0;
+    for (int b = p - 54; b >= 0; --b)
+        sticky |= (int)QBIT(b);
+#undef QBIT
+    if (guard && (sticky || (mant & 1u)))
+        ++mant;
+    /* mant = 2^53 after a carry out is still exact in double */
+    double q = ldexp((double)mant, p - 52 - 149 - 96);
+    return sign < 0 ? -q : q;
+}
+
 /* Per-channel mean of the chunk's keys ([DR] inference: keys are
  * K-smoothed before NVFP4 quantization; the pages give no formula, READING:
  * subtract the per-channel mean over the chunk's tokens).  K is [T, HD]
- * (HD = heads * head_dim, token-major).  The sum is taken in double, in a
- * fixed order (READING; the pages fix none): tokens in tiles of 16, each
- * tile summed in token order from +0; the tile sums, padded with zeros to a
- * power-of-two count, added pairwise level by level (adjacent pairs);
- * mu = (float)(S / T). */
+ * (HD = heads * head_dim, token-major).  mu = (float)RN64(S / T), where S is
+ * the exact sum of the channel's T values (no rounding, so no summation
+ * order enters), S / T is rounded once to double and that double once to
+ * float (READING: the mean is formed in double, as a double sum would give
+ * it whenever that sum is exact).  T < 2^31. */
 void orc_kv_mean(const float *K, int64_t T, int64_t HD, float *mu)
 {
-    const int64_t ntiles = (T + 15) / 16;
-    int64_t npad = 1;
-    while (npad < ntiles)
-        npad *= 2;
-    double *tile = (double *)malloc((size_t)npad * sizeof(double) + 1);
+    int64_t *acc = (int64_t *)calloc((size_t)(HD > 0 ? HD : 1) * KM_DIGITS, sizeof(int64_t));
+    if (!acc)
+        abort();
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t ch = 0; ch < HD; ++ch)
+            exact_add(acc + ch * KM_DIGITS, K[t * HD + ch]);
     for (int64_t ch = 0; ch < HD; ++ch) {
-        for (int64_t p = 0; p < npad; ++p) {
-            double P = 0.0;
-            for (int64_t t = 16 * p; t < 16 * p + 16 && t < T; ++t)
-                P += (double)K[t * HD + ch];
-            tile[p] = P;
-        }
-        for (int64_t n = npad; n > 1; n /= 2)
-            for (int64_t i = 0; i < n / 2; ++i)
-                tile[i] = tile[2 * i] + tile[2 * i + 1];
-        mu[ch] = (T > 0) ? (float)(tile[0] / (double)T) : 0.0f;
+        uint32_t mag[KM_DIGITS];
+        int sign = exact_magnitude(acc + ch * KM_DIGITS, mag);
+        mu[ch] = (T > 0) ? (float)exact_quotient(sign, mag, (uint32_t)T) : 0.0f;
     }
-    free(tile);
+    free(acc);
 }
 
 /* Quantize one KV chunk independently ([DR]: chunk-level, F_c = 8 frames;

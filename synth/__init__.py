@@ -103,14 +103,27 @@ def weights(seed: int, operand: int, rows: int, cols: int, std: float = 0.02) ->
     return (normal(seed, operand, rows * cols) * std).astype(np.float32).reshape(rows, cols)
 
 
-def kv_chunk(seed: int, chunk: int, tokens: int, heads: int, head_dim: int, token_start: int = 0):
+def kv_chunk(seed: int, chunk: int, tokens: int, heads: int, head_dim: int, token_start: int = 0,
+             threads: int = 1):
     """One KV chunk as bf16 bit arrays [tokens, heads, head_dim].
 
     K = N(0,1) + bias[c], bias ~ N(0, 4) drawn once per channel c of the head
     dimension and shared by all heads and chunks (channel outliers).
     V = N(0,1).  ``token_start`` lets a caller draw a sub-range of tokens
-    (the same values the full chunk would hold there).
+    (the same values the full chunk would hold there).  ``threads`` > 1 draws
+    token ranges on that many threads (numpy releases the GIL in its array
+    loops); every element is a function of its index, so the result is the
+    same.
     """
+    if threads > 1 and tokens >= 2 * threads:
+        from concurrent.futures import ThreadPoolExecutor
+
+        cuts = [tokens * i // threads for i in range(threads + 1)]
+        with ThreadPoolExecutor(threads) as ex:
+            parts = list(ex.map(lambda i: kv_chunk(seed, chunk, cuts[i + 1] - cuts[i], heads,
+                                                   head_dim, token_start + cuts[i]),
+                                range(threads)))
+        return (np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]))
     hd = heads * head_dim
     bias = normal(seed, 999, head_dim) * 2.0
     start = token_start * hd
@@ -118,6 +131,18 @@ def kv_chunk(seed: int, chunk: int, tokens: int, heads: int, head_dim: int, toke
     k = normal(seed, 2 * chunk + 10, n, start).reshape(tokens, heads, head_dim) + bias[None, None, :]
     v = normal(seed, 2 * chunk + 11, n, start).reshape(tokens, heads, head_dim)
     return to_bf16_bits(k.astype(np.float32)), to_bf16_bits(v.astype(np.float32))
+
+
+def host_threads() -> int:
+    """Worker threads for host-side generation and the oracle: the CPUs this
+    process may run on, at most 16."""
+    import os
+
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 # Shapes of the LongLive-2.0 5B model as used by the workloads.

@@ -129,3 +129,23 @@ def rocm_encode(fn_name: str, x: np.ndarray) -> np.ndarray:
     out = np.empty(x.shape, np.uint8)
     getattr(L, fn_name)(x.ctypes.data, x.size, out.ctypes.data)
     return out
+
+
+def kmean_fp64_exact(K: np.ndarray) -> bool:
+    """True if, for every channel (column) of K, a sum of its values in double
+    is exact in any order: each nonzero value is an odd multiple of 2^k for
+    some k >= k_min, so every partial sum is an integer multiple of 2^k_min
+    no larger in magnitude than sum |v|; below 2^53 * 2^k_min such a multiple
+    is a double.  (The kernels' key-mean sums are exact, and so equal the
+    oracle's exact mean, on such inputs.)"""
+    K = np.ascontiguousarray(K, np.float32)
+    u = K.view(np.uint32)
+    be = ((u >> np.uint32(23)) & np.uint32(0xFF)).astype(np.int32)
+    M = (u & np.uint32(0x7FFFFF)).astype(np.int32)
+    M |= np.where(be > 0, np.int32(0x800000), np.int32(0))  # value = +-M * 2^(max(be, 1) - 150)
+    low = M & -M                                           # lowest set bit of M (a power of two)
+    lexp = (low.astype(np.float32).view(np.int32) >> 23) - 127
+    k = np.where(M != 0, lexp + np.maximum(be, 1) - 150, np.int32(1 << 20))
+    kmin = k.min(axis=0).astype(np.int64)
+    s = np.abs(K).sum(axis=0, dtype=np.float64) * (1.0 + 1e-9)
+    return bool(np.all(s < np.ldexp(1.0, np.minimum(53 + kmin, 1000))))

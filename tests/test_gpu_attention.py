@@ -191,6 +191,40 @@ def test_attention_64s_ring_step_15_sampled(nv, orc):
     check(nv, orc, ring, chunks, cfg, 15, 10, qbits, qf, rows=rows, key_splits=(0, 1))
 
 
+@pytest.mark.parametrize("key_splits", [1, 3, 8])
+def test_attention_identical_values_reproduced(nv, orc, key_splits):
+    """Every token of every chunk carries the same value row: the softmax
+    weights, whatever they are, then average identical rows, and o must be
+    that row exactly (bf16).  The kernel divides the bf16-rounded weights'
+    value product by the sum of the same rounded weights, so o is an exact
+    weighted mean up to fp32 summation; a normaliser of unrounded weights
+    would scale o by up to 1 +- 2^-9 and move it off the row.  (A -0 value
+    comes back as +0: the sums start from +0.)"""
+    cfg = small_cfg(nv)
+    Tc, H, d = cfg.chunk_tokens, cfg.heads, cfg.head_dim
+    qbits, _ = queries(3011, 200, H, d)
+    _, vrow = synth.kv_chunk(3012, 0, 1, H, d)
+    vb = np.ascontiguousarray(np.broadcast_to(vrow, (Tc, H, d)))
+    ring = nv.KVRing(cfg)
+    vhat = None
+    for t in range(6):
+        if t in (0, 4):
+            ring.begin_shot(t)
+        kb, _ = synth.kv_chunk(3013, t, Tc, H, d)
+        ring.store_chunk(t, bf16_gpu(kb, (Tc, H, d)), bf16_gpu(vb, (Tc, H, d)))
+        if vhat is None:
+            enc = orc.kv_encode_chunk(f32_of_bits(kb).reshape(Tc, H * d),
+                                      f32_of_bits(vb).reshape(Tc, H * d))
+            vhat = orc.kv_dequant_tokens(enc, 0, 1, key=False).reshape(H, d)
+    print("case: attention identical values, splits", key_splits, flush=True)
+    q = bf16_gpu(qbits, (200, H, d))
+    for scale in (d ** -0.5, 0.7):
+        o = ring.attention(6, q, scale, key_splits=key_splits)
+        torch.cuda.synchronize()
+        of = o.float().cpu().numpy()
+        assert np.array_equal(of, np.broadcast_to(f32_of_bits(vhat), of.shape)), (scale, key_splits)
+
+
 @pytest.mark.parametrize("key_splits", [1, 3])
 def test_attention_deterministic(nv, orc, key_splits):
     """Fixed tile order, fixed in-tile order and a fixed merge order: two

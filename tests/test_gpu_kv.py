@@ -7,8 +7,10 @@ import pytest
 import torch
 
 import synth
+from helpers import kmean_fp64_exact
 
 pytestmark = pytest.mark.gpu
+THREADS = synth.host_threads()
 
 
 @pytest.fixture(scope="module")
@@ -20,11 +22,15 @@ def nv():
 
 
 def chunk_inputs(seed, c, T, H, d):
-    kb, vb = synth.kv_chunk(seed, c, T, H, d)
+    kb, vb = synth.kv_chunk(seed, c, T, H, d, threads=THREADS)
     Kg = torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16).cuda()
     Vg = torch.from_numpy(vb.view(np.int16)).view(torch.bfloat16).cuda()
     K = synth.bf16_bits_to_f32(kb).reshape(T, H * d)
     V = synth.bf16_bits_to_f32(vb).reshape(T, H * d)
+    # the kernels' double key sums are exact (so equal the oracle's exact
+    # mean) on inputs like these; the library leaves other inputs' mean
+    # unspecified up to that rounding
+    assert kmean_fp64_exact(K), f"chunk {c} of seed {seed} outside the key-mean domain"
     return Kg, Vg, K, V
 
 
@@ -32,7 +38,9 @@ def bf16_np(t):
     return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16).reshape(t.shape[0], -1)
 
 
-def run_ring(nv, orc, cfg, cuts, steps, seed, full_check=True, sample_tokens=None):
+def run_ring(nv, orc, cfg, cuts, steps, seed):
+    """Drive the ring through `steps` steps (shot cuts at `cuts`) and compare
+    every gathered value with the oracle's gather."""
     ring = nv.KVRing(cfg)
     Tc, H, d = cfg.chunk_tokens, cfg.heads, cfg.head_dim
     g_tok = cfg.sink_frames_global * cfg.tokens_per_frame
@@ -48,25 +56,14 @@ def run_ring(nv, orc, cfg, cuts, steps, seed, full_check=True, sample_tokens=Non
         toks = orc.effective_tokens(t, Tc, cfg.window_chunks, g_tok, shot * Tc, s_tok)
         assert Kw.shape[0] == len(toks), (t, Kw.shape, len(toks))
         if len(toks):
-            if full_check:
-                _, Kr, Vr = orc.gather_window(chunks, t, Tc, cfg.window_chunks, g_tok, shot * Tc,
-                                              s_tok)
-                kg, vg = bf16_np(Kw), bf16_np(Vw)
-                assert np.array_equal(kg, Kr), f"step {t}: K differs"
-                assert np.array_equal(vg, Vr), f"step {t}: V differs"
-            else:
-                idx = np.unique(np.concatenate([[0, len(toks) - 1],
-                                                np.random.default_rng(t).integers(0, len(toks), sample_tokens)]))
-                kg, vg = bf16_np(Kw[idx]), bf16_np(Vw[idx])
-                for j, i in enumerate(idx):
-                    tok = int(toks[i])
-                    c = tok // Tc
-                    kr = orc.kv_dequant_tokens(chunks[c], tok - c * Tc, 1, key=True)
-                    vr = orc.kv_dequant_tokens(chunks[c], tok - c * Tc, 1, key=False)
-                    assert np.array_equal(kg[j], kr[0]) and np.array_equal(vg[j], vr[0]), (t, tok)
+            _, Kr, Vr = orc.gather_window(chunks, t, Tc, cfg.window_chunks, g_tok, shot * Tc,
+                                          s_tok)
+            kg, vg = bf16_np(Kw), bf16_np(Vw)
+            assert np.array_equal(kg, Kr), f"step {t}: K differs"
+            assert np.array_equal(vg, Vr), f"step {t}: V differs"
         Kg, Vg, K, V = chunk_inputs(seed, t, Tc, H, d)
         ring.store_chunk(t, Kg, Vg)
-        chunks[t] = orc.kv_encode_chunk(K, V, search=cfg.search)
+        chunks[t] = orc.kv_encode_chunk(K, V, search=cfg.search, threads=THREADS)
         # drop chunks no step can reference any more (window and sinks)
         for old in list(chunks):
             if old not in (0, shot) and old < t + 1 - cfg.window_chunks:
@@ -118,6 +115,7 @@ STORE_CASES = [
     (520, 8, 2, 128, 3, 3),
     (880, 8, 3, 128, 3, 3),
     (8192, 8, 1, 16, 1, 1),
+    (880, 8, 24, 128, 3, 3),  # the 5B model's whole chunk: 7040 tokens x 24 heads x 128
 ]
 
 
@@ -133,7 +131,7 @@ def test_store_bit_exact_ragged_and_sinks(nv, orc, case):
     ring = nv.KVRing(cfg)
     Kg, Vg, K, V = chunk_inputs(2100 + T, 0, T, H, d)
     ring.store_chunk(0, Kg, Vg)
-    ref = orc.kv_encode_chunk(K, V)
+    ref = orc.kv_encode_chunk(K, V, threads=THREADS)
     mem = ring_bytes(ring)
     assert_region(region(mem, 0, T, HD), ref, T, HD)
     if Sg:
@@ -195,12 +193,73 @@ def test_ring_64s_schedule_one_head(nv, orc):
     run_ring(nv, orc, cfg, cuts={0, 10, 20, 30}, steps=40, seed=1005)
 
 
-def test_ring_full_geometry_sampled(nv, orc):
-    """Full chunk geometry (7040 x 24 x 128) for 7 steps (global sink leaves the
-    window at step 5), sampled gathered tokens checked."""
-    print("case: ring full geometry 7 steps", flush=True)
+def sample_plan(cfg, cuts, steps, n_sample, rng_seed):
+    """Per step t, the positions of E(t) to check (first, last, both sides of
+    every segment boundary, and n_sample random ones), and per chunk the
+    local tokens any step will check."""
+    Tc, W = cfg.chunk_tokens, cfg.window_chunks
+    g_tok = cfg.sink_frames_global * cfg.tokens_per_frame
+    s_tok = cfg.sink_frames_shot * cfg.tokens_per_frame
+    import oracle as orc
+
+    plan, need, shot = {}, {}, 0
+    for t in range(steps):
+        if t in cuts:
+            shot = t
+        toks = orc.effective_tokens(t, Tc, W, g_tok, shot * Tc, s_tok)
+        if len(toks) == 0:
+            plan[t] = (toks, np.zeros(0, np.int64))
+            continue
+        jumps = np.flatnonzero(np.diff(toks) != 1)
+        edges = np.concatenate([[0, len(toks) - 1], jumps, jumps + 1,
+                                np.flatnonzero(np.diff(toks // Tc) != 0) + 1])
+        rnd = np.random.default_rng(rng_seed + t).integers(0, len(toks), n_sample)
+        idx = np.unique(np.concatenate([edges, rnd]))
+        plan[t] = (toks, idx)
+        for tok in toks[idx]:
+            need.setdefault(int(tok // Tc), set()).add(int(tok % Tc))
+    return plan, {c: np.array(sorted(v), np.int64) for c, v in need.items()}
+
+
+def test_ring_64s_schedule_24_heads_sampled(nv, orc):
+    """The 64 s schedule at full geometry (40 chunks of 7040 tokens x 24 heads
+    x 128, cuts every 10 chunks, 3-frame sinks, W = 4): every step's gather
+    on at least 256 sampled tokens plus every segment edge, against the
+    oracle's encoding of each chunk (statistics over the whole chunk)."""
     cfg = nv.KVConfig()
-    run_ring(nv, orc, cfg, cuts={0}, steps=7, seed=1002, full_check=False, sample_tokens=48)
+    cuts = {0, 10, 20, 30}
+    steps, seed = 40, 1005
+    Tc, H, d = cfg.chunk_tokens, cfg.heads, cfg.head_dim
+    plan, need = sample_plan(cfg, cuts, steps, 256, 6400)
+    ring = nv.KVRing(cfg)
+    enc = {}  # chunk -> (oracle encoding of its needed tokens, token -> row)
+    for t in range(steps):
+        print("case: ring 64s 24 heads step", t, flush=True)
+        if t in cuts:
+            ring.begin_shot(t)
+        Kw, Vw = ring.gather_window(t)
+        toks, idx = plan[t]
+        assert Kw.shape[0] == len(toks), (t, Kw.shape, len(toks))
+        if len(idx):
+            sel = torch.from_numpy(idx).cuda()
+            kg, vg = bf16_np(Kw[sel]), bf16_np(Vw[sel])
+            for j, i in enumerate(idx):
+                tok = int(toks[i])
+                c, local = tok // Tc, tok % Tc
+                ch, row = enc[c]
+                r = row[local]
+                kr = orc.kv_dequant_tokens(ch, r, 1, key=True)
+                vr = orc.kv_dequant_tokens(ch, r, 1, key=False)
+                assert np.array_equal(kg[j], kr[0]), f"step {t} token {tok}: K differs"
+                assert np.array_equal(vg[j], vr[0]), f"step {t} token {tok}: V differs"
+        Kg, Vg, K, V = chunk_inputs(seed, t, Tc, H, d)
+        ring.store_chunk(t, Kg, Vg)
+        rows = need.get(t, np.zeros(0, np.int64))
+        if len(rows):
+            enc[t] = (orc.kv_encode_chunk(K, V, threads=THREADS, rows=rows),
+                      {int(v): k for k, v in enumerate(rows)})
+        del Kg, Vg, K, V
+    torch.cuda.synchronize()
 
 
 def test_gather_capacity_error(nv):

@@ -204,3 +204,36 @@ def test_shape_errors(orc):
         orc.quantize(np.zeros((4, 24), np.float32))
     with pytest.raises(ValueError):
         orc.quantize(np.zeros((8, 32), np.float32), layout=orc.LAYOUT_2D)
+
+
+# Blocks whose two candidates tie exactly, with distinct block scales
+# (tensor scale pinned to s_enc = s_dec = 1 by amax = 2688).  Derived by hand:
+#   [6, 1.25, 0...]: target 6 gives scale 1.0 (E4M3 0x38), codes 6 -> 0x7,
+#     1.25 -> 1.0 (the midpoint of 1 and 1.5 goes to the even code 0x2),
+#     error (1/4)^2; target 4 gives scale 1.5 (0x3C), 6 -> 4 * 1.5 (0x6),
+#     1.25 * RN(1/1.5) = 0.8333 -> 1.0 * 1.5 (0x2), error (1/4)^2 as well.
+#   [6, -3, 1.5, 0...]: both candidates reproduce every value (error 0).
+# The rule keeps target 6 on a tie, so both blocks take scale 0x38.
+TIE_BLOCKS = [
+    ([6.0, 1.25], 0.0625, [0x27] + [0] * 7),
+    ([6.0, -3.0, 1.5], 0.0, [0xD7, 0x03] + [0] * 6),
+]
+
+
+def tie_block(vals):
+    x = np.zeros((1, 16), np.float32)
+    x[0, :len(vals)] = vals
+    return x
+
+
+@pytest.mark.parametrize("vals,err,codes", TIE_BLOCKS, ids=["tie_nonzero", "tie_zero"])
+def test_four_over_six_tie_keeps_six(orc, vals, err, codes):
+    x = tie_block(vals)
+    c, s, d, e6, e4 = orc.quantize(x, amax=2688.0, return_errors=True)
+    assert d == 1.0
+    assert e6[0, 0] == e4[0, 0] == np.float32(err)
+    assert s[0, 0] == 0x38, hex(s[0, 0])
+    assert list(c[0]) == codes
+    # 2-D: sixteen identical rows tie the same way (tree sums of equal row errors)
+    c2, s2, _ = orc.quantize(np.repeat(x, 16, axis=0), layout=orc.LAYOUT_2D, amax=2688.0)
+    assert s2[0, 0] == 0x38 and all(list(r) == codes for r in c2)
