@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 1
+#define NVFP4_ABI_VERSION 2
 
 typedef enum nvfp4_status {
     NVFP4_OK = 0,
@@ -327,15 +327,27 @@ int nvfp4_kv_begin_shot(nvfp4_kv_ring *ring, int64_t chunk_idx);
  *   largest power of two dividing every nonzero key of the channel (for
  *   bf16 keys it suffices that their exponents span at most 45 - log2(T_c)
  *   binades: 32 at T_c = 7040); outside that domain mu may differ from it
- *   in the last bit.  K_s and V are each quantized 1-D along (h, c) with one FP32
- *   tensor scale per chunk.  Chunk 0 also fills the global-sink region and
- *   the first chunk of a shot fills the shot-sink region (byte copies of the
- *   leading sink tokens, written by the same kernel).  Advances next_chunk.
- * Workspace: device, >= nvfp4_kv_store_workspace_bytes().
+ *   in the last bit.  K_s and V are each quantized 1-D along (h, c) with one
+ *   FP32 tensor scale per chunk.  Chunk 0 also fills the global-sink region
+ *   and the first chunk of a shot fills the shot-sink region (byte copies of
+ *   the leading sink tokens, written by the same kernel).  Advances
+ *   next_chunk.
+ *   v_amax_in: NULL, or a device fp32 holding max |V| over the chunk, as a
+ *   fused producer has it (e.g. the amax_out of the GEMM that wrote V; the
+ *   same applies as for nvfp4_quantize's amax_in): the value tensor scale
+ *   then comes from it and the statistics pass reads the keys only.  Another
+ *   value is used as given (values beyond it saturate as in nvfp4_quantize).
+ * Workspace: device, >= nvfp4_kv_store_workspace_bytes(), 16-byte aligned,
+ *   owned by the caller.  It holds accumulators that must be zero when the
+ *   store of a chunk > 0 starts: every store leaves them zero, and the store
+ *   of chunk 0 clears them first (one small extra launch).  So one workspace
+ *   serves one ring's stores, or several rings' stores one after another;
+ *   two stores sharing a workspace must not overlap.
+ * Three launches (four for chunk 0): statistics, finalize, encode.
  */
 int nvfp4_kv_store_chunk(nvfp4_kv_ring *ring, int64_t chunk_idx, const void *K_bf16,
-                         const void *V_bf16, void *workspace, size_t workspace_bytes,
-                         void *stream);
+                         const void *V_bf16, const float *v_amax_in, void *workspace,
+                         size_t workspace_bytes, void *stream);
 
 /*
  * Number of tokens in K_eff(step) (step must equal ring->next_chunk: the

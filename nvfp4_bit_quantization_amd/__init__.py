@@ -92,7 +92,7 @@ _EXPORTS = {
                            C.c_int),
     "nvfp4_kv_begin_shot": ([C.POINTER(CKvRing), C.c_int64], C.c_int),
     "nvfp4_kv_store_chunk": ([C.POINTER(CKvRing), C.c_int64, C.c_void_p, C.c_void_p,
-                              C.c_void_p, C.c_size_t, C.c_void_p], C.c_int),
+                              C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p], C.c_int),
     "nvfp4_kv_effective_tokens": ([C.POINTER(CKvRing), C.c_int64, C.POINTER(C.c_int64)],
                                   C.c_int),
     "nvfp4_gather_window": ([C.POINTER(CKvRing), C.c_int64, C.c_void_p, C.c_void_p, C.c_int64,
@@ -414,7 +414,8 @@ class KVRing:
         self.mem = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
         off = (-self.mem.data_ptr()) % 256
         self._base = self.mem.data_ptr() + off
-        self.ws = torch.empty(kv_store_workspace_bytes(cfg), dtype=torch.uint8, device=device)
+        # zero-filled; every store leaves it so (the first store clears it too)
+        self.ws = torch.zeros(kv_store_workspace_bytes(cfg), dtype=torch.uint8, device=device)
         self.ring = CKvRing()
         _check(lib().nvfp4_kv_ring_init(C.byref(self.ring), C.byref(c), C.c_void_p(self._base),
                                         nbytes))
@@ -426,15 +427,19 @@ class KVRing:
     def begin_shot(self, chunk_idx: int):
         _check(lib().nvfp4_kv_begin_shot(C.byref(self.ring), chunk_idx))
 
-    def store_chunk(self, chunk_idx: int, K: torch.Tensor, V: torch.Tensor, stream=None):
+    def store_chunk(self, chunk_idx: int, K: torch.Tensor, V: torch.Tensor,
+                    v_amax: torch.Tensor | None = None, stream=None):
+        """nvfp4_kv_store_chunk; v_amax (optional one-element float32 device
+        tensor): max|V| over the chunk from its producer."""
         if K.dtype != torch.bfloat16 or V.dtype != torch.bfloat16:
             raise ValueError("K and V must be bfloat16")
         T, hd = self.cfg.chunk_tokens, self.cfg.heads * self.cfg.head_dim
         if K.numel() != T * hd or V.numel() != T * hd:
             raise ValueError(f"K and V must hold [{T}, {self.cfg.heads}, {self.cfg.head_dim}]")
         _check(lib().nvfp4_kv_store_chunk(C.byref(self.ring), chunk_idx, _dev(K, "K"),
-                                          _dev(V, "V"), C.c_void_p(self.ws.data_ptr()),
-                                          self.ws.numel(), _stream(stream)))
+                                          _dev(V, "V"), _amax_arg(v_amax, "v_amax"),
+                                          C.c_void_p(self.ws.data_ptr()), self.ws.numel(),
+                                          _stream(stream)))
 
     def effective_tokens(self, step: int) -> int:
         n = C.c_int64()

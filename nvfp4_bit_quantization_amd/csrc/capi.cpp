@@ -449,8 +449,8 @@ int nvfp4_kv_begin_shot(nvfp4_kv_ring *ring, int64_t chunk_idx) {
 }
 
 int nvfp4_kv_store_chunk(nvfp4_kv_ring *ring, int64_t chunk_idx, const void *K_bf16,
-                         const void *V_bf16, void *workspace, size_t workspace_bytes,
-                         void *stream) {
+                         const void *V_bf16, const float *v_amax_in, void *workspace,
+                         size_t workspace_bytes, void *stream) {
     int st = check_ring(ring);
     if (st) return st;
     if (chunk_idx != ring->next_chunk)
@@ -459,6 +459,8 @@ int nvfp4_kv_store_chunk(nvfp4_kv_ring *ring, int64_t chunk_idx, const void *K_b
     if (!K_bf16 || !V_bf16) return fail(NVFP4_EINVAL, "kv_store_chunk: NULL K or V");
     if (!aligned16(K_bf16) || !aligned16(V_bf16) || !aligned16(workspace))
         return fail(NVFP4_EALIGN, "kv_store_chunk: K, V and workspace must be 16-byte aligned");
+    if ((uintptr_t)v_amax_in & 3u)
+        return fail(NVFP4_EALIGN, "kv_store_chunk: v_amax_in misaligned");
     const size_t need = nvfp4_kv_store_workspace_bytes(&ring->cfg);
     if (!workspace || workspace_bytes < need)
         return fail(NVFP4_ENOSPC, "kv_store_chunk: workspace %zu < %zu bytes", workspace_bytes,
@@ -479,7 +481,9 @@ int nvfp4_kv_store_chunk(nvfp4_kv_ring *ring, int64_t chunk_idx, const void *K_b
     a.ssink = region_at(ring->base + ring->ssink_offset, region_layout(stok, hd));
     a.g_tokens = (chunk_idx == 0) ? gtok : 0;
     a.s_tokens = (chunk_idx * T == ring->s_start) ? stok : 0;
+    a.v_amax_in = v_amax_in;
     a.ws = workspace;
+    a.clear_ws = (chunk_idx == 0);
     hipError_t e = nvfp4::launch_kv_store(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "kv_store_chunk launch");
     ring->next_chunk = chunk_idx + 1;

@@ -12,17 +12,20 @@
 // uses micro-block scaling with the Four Over Six selection.
 //
 // Store = three launches:
-//   kv_stats     two waves per (64-token node, 512 channels): per-channel fp64
-//                tile sums (token order) combined up to the 64-token node,
-//                key max/min, value |max|
-//   kv_finalize  one wave per 16 channels: mu = (float)(sum of tile sums / T)
-//                by the pairwise tree, and the key amax
-//                max_c max(RN(max K - mu), RN(mu - min K)) (equal to the
-//                elementwise amax of RN(K - mu) because RN is monotone)
-//   kv_encode    reduces the amax partials to the FP32 tensor scales of K_s
-//                and V, then the 1-D 4/6 encoder over K_s = RN(K - mu) and V,
-//                writing the ring slot and, for sink chunks, the sink copy in
-//                the same pass
+//   kv_stats     two waves per (64-token node, 512 channels): per-channel key
+//                sums in double, key max / min and the value |max| over the
+//                node, added into the workspace with device-scope atomics
+//                (the sums are exact on the key-mean domain, so their order
+//                does not matter)
+//   kv_finalize  one workgroup per 512-channel group: mu = (float)(S / T),
+//                the group's key amax max_c max(RN(max K - mu), RN(mu - min K))
+//                (equal to the elementwise amax of RN(K - mu) because RN is
+//                monotone) and value amax, and the accumulators cleared for
+//                the next call
+//   kv_encode    the FP32 tensor scales of K_s and V from the groups'
+//                amaxes, then the 1-D 4/6 encoder over K_s = RN(K - mu) and
+//                V, writing the ring slot and, for sink chunks, the sink copy
+//                in the same pass
 // Gather = one launch: one workgroup-iteration per kGatherTok output tokens,
 // one lane per 16-element block; each token's segment (ring slot or sink
 // copy) is found from scalars (sink lengths, window start, W).
@@ -31,70 +34,63 @@
 
 namespace nvfp4 {
 
-// Key-mean summation order (fixed, so the result is reproducible): tokens in
-// tiles of kSeq = 16, each tile summed in token order in double; the tile
-// sums, padded with zeros to a power-of-two count, added pairwise level by
-// level.  kv_stats computes the tile sums and the first two tree levels (one
-// workgroup = 2 waves = 4 consecutive tiles); kv_finalize finishes the tree.
-constexpr int kSeq = 16;            // tokens summed sequentially by one lane
-constexpr int kStatsTokens = 64;    // tokens per stats unit (4 tiles of 16)
-constexpr int kGroupCh = 512;       // channels per stats unit (64 lanes x 8)
-constexpr int kFinCh = 16;          // channels per finalize wave
+constexpr int kStatsTokens = 64;      // tokens per stats unit (two waves of 32)
+constexpr int kGroupCh = 512;         // channels per stats unit (64 lanes x 8)
+constexpr int kHalf = kStatsTokens / 2;  // tokens per stats wave
 constexpr int64_t kEncodeGrid = 4096; // encode workgroups per tensor (upper bound)
 constexpr int64_t kEncodeBlocks = 6;  // target blocks per encode lane (measured: 6 over ~10)
 
+// Store workspace.  The accumulators are zero between calls: every store
+// leaves them so (kv_finalize clears them), and a store of chunk 0 clears
+// them first.
 struct KvWs {
-    double *P;      // [nt64, HD]  level-2 tree nodes (64-token sums)
-    float *kmax;    // [nt64, HD]
-    float *kmin;    // [nt64, HD]
-    float *vpart;   // [nt64 * gy] value |max| per stats unit
-    float *kpart;   // [nfin]      key amax per finalize wave
-};
-
-struct KvDims {
-    int64_t nt64;   // stats units along tokens (64-token nodes)
-    int64_t gy;     // stats units along channels
-    int64_t n2;     // level-2 nodes in the padded tree (power of two)
-    int64_t nfin;   // finalize waves (one workgroup each)
+    double *sum;     // [HD] per-channel key sums
+    uint32_t *kmax;  // [HD] order-preserving bits of the channel's key max
+    uint32_t *kneg;  // [HD] order-preserving bits of minus the channel's key min
+    uint32_t *vmax;  // [gy] value |max| of each channel group (float bits)
+    float *gamax;    // [gy] this call's key amax of each channel group (read by kv_encode)
+    float *gvmax;    // [gy] this call's value amax of each channel group
 };
 
 static inline int64_t align256(int64_t b) { return (b + 255) & ~(int64_t)255; }
 
-static KvDims kv_dims(int64_t T, int64_t HD) {
-    KvDims d;
-    d.nt64 = (T + kStatsTokens - 1) / kStatsTokens;
-    d.gy = (HD + kGroupCh - 1) / kGroupCh;
-    const int64_t nt16 = (T + kSeq - 1) / kSeq;
-    int64_t npad = 1;
-    while (npad < nt16) npad *= 2;
-    d.n2 = npad >= 4 ? npad / 4 : 1;
-    d.nfin = (HD + kFinCh - 1) / kFinCh;
-    return d;
-}
-
-static KvWs carve_ws(void *ws, int64_t T, int64_t HD) {
-    const KvDims d = kv_dims(T, HD);
+static KvWs carve_ws(void *ws, int64_t HD) {
+    const int64_t gy = (HD + kGroupCh - 1) / kGroupCh;
     uint8_t *p = (uint8_t *)ws;
     KvWs w;
-    w.P = (double *)p;
-    p += align256(d.nt64 * HD * 8);
-    w.kmax = (float *)p;
-    p += align256(d.nt64 * HD * 4);
-    w.kmin = (float *)p;
-    p += align256(d.nt64 * HD * 4);
-    w.vpart = (float *)p;
-    p += align256(d.nt64 * d.gy * 4);
-    w.kpart = (float *)p;
+    w.sum = (double *)p;
+    p += align256(HD * 8);
+    w.kmax = (uint32_t *)p;
+    p += align256(HD * 4);
+    w.kneg = (uint32_t *)p;
+    p += align256(HD * 4);
+    w.vmax = (uint32_t *)p;
+    p += align256(gy * 4);
+    w.gamax = (float *)p;
+    p += align256(gy * 4);
+    w.gvmax = (float *)p;
     return w;
 }
 
+// The part that must be zero between calls, and the whole.
+static int64_t kv_ws_zero_bytes(int64_t HD) {
+    const int64_t gy = (HD + kGroupCh - 1) / kGroupCh;
+    return align256(HD * 8) + 2 * align256(HD * 4) + align256(gy * 4);
+}
 size_t kv_store_ws_bytes(int64_t T, int64_t HD) {
-    const KvDims d = kv_dims(T, HD);
-    return (size_t)(align256(d.nt64 * HD * 8) + 2 * align256(d.nt64 * HD * 4) +
-                    align256(d.nt64 * d.gy * 4) + align256(d.nfin * 4));
+    (void)T;
+    const int64_t gy = (HD + kGroupCh - 1) / kGroupCh;
+    return (size_t)(kv_ws_zero_bytes(HD) + 2 * align256(gy * 4));
 }
 
-constexpr int kHalf = kStatsTokens / 2;  // tokens per stats wave (two tiles)
+// Bits of a float whose unsigned order is the float order (-0 just below +0).
+__device__ __forceinline__ uint32_t ord_bits(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float ord_value(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
 
 // The 32 loads of a wave's two tiles (a full node: no token past T) as raw
 // buffer loads: the node's wave-uniform base is in the buffer descriptor,
@@ -143,22 +139,34 @@ __device__ __forceinline__ float stats_value_token(const u32x4 &r, float m) {
 }
 
 // Workgroup = 2 waves = one unit (64-token node p, 512-channel group y);
-// blockIdx.y selects keys (0) or values (1).  Wave h takes tokens
-// 64 p + 32 h .. +31; lane l owns channels 512 y + 8 l .. +7 (one 16-byte
-// load per token), and all 32 loads of a wave are issued before any is
-// used.  Keys: each 16-token tile is summed in token order in double; the
-// wave adds its two tile sums (tree level 1), wave 1 hands its node to wave
-// 0 through LDS, which adds them (level 2) and stores the level-2 node with
-// the per-channel max / min.  Values: the |max| of the unit.  The last,
-// partial node reads token by token up to T; its absent tiles are +0, the
-// value the padded tree gives them.
+// blockIdx.y selects keys (0) or values (1; absent when the caller supplies
+// the value amax).  Wave h takes tokens 64 p + 32 h .. +31; lane l owns
+// channels 512 y + 8 l .. +7 (one 16-byte load per token), and all 32 loads
+// of a wave are issued before any is used; the last, partial node reads
+// token by token up to T.  Keys: per-channel double sums, max and min over
+// the wave's tokens; both waves put theirs in LDS and the workgroup adds
+// the unit's 512 channels to the workspace with atomics, thread t taking
+// channels t + 128 j so that one atomic instruction covers consecutive
+// addresses (atomic add of the sums, atomic max of the order-preserving
+// bits of max and of -min; measured: lane-strided atomics cost 30 us a
+// chunk, consecutive ones 2 us).  Values: the unit's |max|, one atomic max
+// into its channel group's word.  Each double sum and every partial sum
+// the atomics form is exact on the key-mean domain (every partial sum of a
+// channel's keys is a multiple of the channel's smallest key unit below
+// 2^53 of them), so mu does not depend on the order in which units arrive.
+// (Measured alternatives to the kv_finalize launch: finalizing in the
+// last-arriving workgroup of each group, found by a ticket counter, 9-10 us
+// slower, since every workgroup then waits for its atomics to be performed
+// before it can take a ticket and retire; finalizing in every kv_encode
+// workgroup's prologue, ~5 us slower, since each key workgroup reads all
+// the channels' statistics and divides for every channel.)
 __global__ __launch_bounds__(128) void kv_stats_kernel(const uint16_t *__restrict__ K,
                                                        const uint16_t *__restrict__ V, int64_t T,
                                                        int64_t HD, int64_t gy, KvWs w) {
-    __shared__ double sp[8][64];
-    __shared__ float sx[8][64];
-    __shared__ float sn[8][64];
-    __shared__ float sv;
+    __shared__ double sp[2][8][64];
+    __shared__ float sx[2][8][64];
+    __shared__ float sn[2][8][64];
+    __shared__ float red[2];
     const int h = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int64_t unit = blockIdx.x;
@@ -187,137 +195,105 @@ __global__ __launch_bounds__(128) void kv_stats_kernel(const uint16_t *__restric
         }
         m = ch_ok ? m : 0.0f;
         m = wave_max(m);
-        if (h == 1 && lane == 0) sv = m;
+        if (lane == 0) red[h] = m;
         __syncthreads();
-        if (h == 0 && lane == 0) w.vpart[unit] = fmaxf(m, sv);
-        return;
-    }
-    double node[8];
-    float mx[8], mn[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        mx[i] = -__builtin_huge_valf();
-        mn[i] = __builtin_huge_valf();
-    }
-    if (full) {
-        u32x4 r[kHalf];
-        stats_load(r, rs, voff, 0, rb);
-        double a[8], b[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) a[i] = b[i] = 0.0;
-#pragma unroll
-        for (int j = 0; j < kSeq; ++j) stats_key_token(r[j], a, mx, mn);
-#pragma unroll
-        for (int j = kSeq; j < kHalf; ++j) stats_key_token(r[j], b, mx, mn);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) node[i] = a[i] + b[i];
+        if (threadIdx.x == 0) atomicMax(&w.vmax[y], __float_as_uint(fmaxf(red[0], red[1])));
     } else {
+        float mx[8], mn[8];
         double a[8], b[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) a[i] = b[i] = 0.0;
-#pragma unroll 1
-        for (int64_t j = 0; j < kSeq && t0 + j < T; ++j)
-            stats_key_token(*(const u32x4 *)(row + j * HD + off), a, mx, mn);
-#pragma unroll 1
-        for (int64_t j = kSeq; j < kHalf && t0 + j < T; ++j)
-            stats_key_token(*(const u32x4 *)(row + j * HD + off), b, mx, mn);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) node[i] = a[i] + b[i];
-    }
-    if (h == 1) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            sp[i][lane] = node[i];
-            sx[i][lane] = mx[i];
-            sn[i][lane] = mn[i];
+            mx[i] = -__builtin_huge_valf();
+            mn[i] = __builtin_huge_valf();
+            a[i] = b[i] = 0.0;
+        }
+        if (full) {
+            u32x4 r[kHalf];
+            stats_load(r, rs, voff, 0, rb);
+#pragma unroll
+            for (int j = 0; j < kHalf / 2; ++j) stats_key_token(r[j], a, mx, mn);
+#pragma unroll
+            for (int j = kHalf / 2; j < kHalf; ++j) stats_key_token(r[j], b, mx, mn);
+        } else {
+#pragma unroll 1
+            for (int64_t j = 0; t0 + j < T; ++j)
+                stats_key_token(*(const u32x4 *)(row + j * HD + off), a, mx, mn);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            sp[h][i][lane] = a[i] + b[i];
+            sx[h][i][lane] = mx[i];
+            sn[h][i][lane] = mn[i];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kGroupCh / 128; ++j) {
+            const int c = (int)threadIdx.x + 128 * j, i = c & 7, l = c >> 3;  // lane l, slot i
+            const int64_t ch = y * kGroupCh + c;
+            if (ch < HD) {
+                unsafeAtomicAdd(&w.sum[ch], sp[0][i][l] + sp[1][i][l]);
+                atomicMax(&w.kmax[ch], ord_bits(fmaxf(sx[0][i][l], sx[1][i][l])));
+                atomicMax(&w.kneg[ch], ord_bits(-fminf(sn[0][i][l], sn[1][i][l])));
+            }
         }
     }
-    __syncthreads();
-    if (h == 1 || !ch_ok) return;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        node[i] = node[i] + sp[i][lane];
-        mx[i] = fmaxf(mx[i], sx[i][lane]);
-        mn[i] = fminf(mn[i], sn[i][lane]);
-    }
-    double *P = w.P + p * HD + chq;
-    float *X = w.kmax + p * HD + chq;
-    float *N = w.kmin + p * HD + chq;
-#pragma unroll
-    for (int i = 0; i < 8; i += 2) *(f64x2 *)(P + i) = f64x2{node[i], node[i + 1]};
-    *(f32x4 *)X = f32x4{mx[0], mx[1], mx[2], mx[3]};
-    *(f32x4 *)(X + 4) = f32x4{mx[4], mx[5], mx[6], mx[7]};
-    *(f32x4 *)N = f32x4{mn[0], mn[1], mn[2], mn[3]};
-    *(f32x4 *)(N + 4) = f32x4{mn[4], mn[5], mn[6], mn[7]};
 }
 
-// Tree sum of 32 doubles, adjacent pairs level by level.
-__device__ __forceinline__ double tree32(double (&v)[32]) {
+// One workgroup per 512-channel group y, two channels a thread (loads issued
+// first): mu = (float)(S / T) into the slot (and the sink copies), the
+// group's key amax max_c max(RN(max K - mu), RN(mu - min K)) and value amax
+// for kv_encode; the group's sums, extrema and value maximum go back to zero
+// for the next call.  The accumulators are read and cleared with
+// device-scope atomic loads and stores (coherent across the chip's L2
+// caches, like the atomics that filled them).
+__global__ __launch_bounds__(256) void kv_finalize_kernel(KvWs w, int64_t T, int64_t HD,
+                                                          float *mu_slot, float *mu_g,
+                                                          float *mu_s) {
+    __shared__ float red[4];
+    constexpr int kPer = kGroupCh / 256;
+    const int64_t y = blockIdx.x;
+    double S[kPer];
+    uint32_t xo[kPer], no[kPer];
 #pragma unroll
-    for (int w = 16; w >= 1; w >>= 1)
+    for (int j = 0; j < kPer; ++j) {
+        int64_t c = y * kGroupCh + (int)threadIdx.x + 256 * j;
+        c = c < HD ? c : HD - 1;
+        S[j] = __hip_atomic_load(&w.sum[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        xo[j] = __hip_atomic_load(&w.kmax[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        no[j] = __hip_atomic_load(&w.kneg[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    float am = 0.0f;
 #pragma unroll
-        for (int i = 0; i < w; ++i) v[i] = v[2 * i] + v[2 * i + 1];
-    return v[0];
+    for (int j = 0; j < kPer; ++j) {
+        const int64_t c = y * kGroupCh + (int)threadIdx.x + 256 * j;
+        if (c < HD) {
+            const float mu = (float)(S[j] / (double)T);
+            mu_slot[c] = mu;
+            if (mu_g) mu_g[c] = mu;
+            if (mu_s) mu_s[c] = mu;
+            // RN(max K - mu) and RN(mu - min K) = RN(mu + (-min K))
+            am = fmaxf(am, fmaxf(ord_value(xo[j]) - mu, mu + ord_value(no[j])));
+            __hip_atomic_store(&w.sum[c], 0.0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&w.kmax[c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&w.kneg[c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    am = wave_max(am);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = am;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t vb = __hip_atomic_load(&w.vmax[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        w.gamax[y] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        w.gvmax[y] = __uint_as_float(vb);
+        __hip_atomic_store(&w.vmax[y], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
-// One wave per 16 channels: lane = (channel c = lane & 15, quarter
-// q = lane >> 4).  The level-2 nodes of a channel form blocks of 32 (nodes
-// past the last 64-token node are zero); quarter q sums blocks q, q + 4, ...
-// with a fixed 32-leaf tree into LDS, then the q = 0 lanes sum the block
-// sums with the same tree (zero padded; adding an exact zero changes
-// nothing, and no partial sum is -0).  This is the level-by-level pairwise
-// tree over the 16-token tile sums.  mu = (float)(S / T); the wave's key
-// amax max_c max(RN(max K - mu), RN(mu - min K)) goes to kpart.
-__global__ __launch_bounds__(64) void kv_finalize_kernel(KvWs w, int64_t nt64, int64_t n2,
-                                                         int64_t T, int64_t HD, float *mu_slot,
-                                                         float *mu_g, float *mu_s) {
-    __shared__ double bs[32][kFinCh];
-    __shared__ float rx[4][kFinCh];
-    __shared__ float rn[4][kFinCh];
-    const int lane = threadIdx.x, c = lane & (kFinCh - 1), q = lane >> 4;
-    const int64_t ch = (int64_t)blockIdx.x * kFinCh + c;
-    const int nb = n2 >= 32 ? (int)(n2 / 32) : 1;  // blocks of 32 nodes (<= 32)
-    float kx = -__builtin_huge_valf(), kn = __builtin_huge_valf();
-    const int64_t chc = ch < HD ? ch : HD - 1;
-    for (int b = q; b < nb; b += 4) {
-        double v[32];
-        float xv[32], nv[32];
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            const int64_t node = (int64_t)b * 32 + i;
-            const int64_t nc = node < nt64 ? node : nt64 - 1;
-            v[i] = w.P[nc * HD + chc];
-            xv[i] = w.kmax[nc * HD + chc];
-            nv[i] = w.kmin[nc * HD + chc];
-        }
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            const bool ok = (int64_t)b * 32 + i < nt64;
-            v[i] = ok ? v[i] : 0.0;
-            kx = ok ? fmaxf(kx, xv[i]) : kx;
-            kn = ok ? fminf(kn, nv[i]) : kn;
-        }
-        bs[b][c] = tree32(v);
-    }
-    rx[q][c] = kx;
-    rn[q][c] = kn;
-    __syncthreads();
-    float amax = 0.0f;
-    if (q == 0 && ch < HD) {
-        double v[32];
-#pragma unroll
-        for (int i = 0; i < 32; ++i) v[i] = (i < nb) ? bs[i][c] : 0.0;
-        const double S = tree32(v);
-        const float mu = (float)(S / (double)T);
-        mu_slot[ch] = mu;
-        if (mu_g) mu_g[ch] = mu;
-        if (mu_s) mu_s[ch] = mu;
-        const float x = fmaxf(fmaxf(rx[0][c], rx[1][c]), fmaxf(rx[2][c], rx[3][c]));
-        const float n = fminf(fminf(rn[0][c], rn[1][c]), fminf(rn[2][c], rn[3][c]));
-        amax = fmaxf(x - mu, mu - n);
-    }
-    amax = wave_max(amax);
-    if (lane == 0) w.kpart[blockIdx.x] = amax;
+// Zero the store workspace (the first store of a ring).
+__global__ __launch_bounds__(256) void kv_ws_clear_kernel(uint32_t *__restrict__ p, int64_t n4) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
 }
 
 // Raw 16-element bf16 block at byte offset `off` of a buffer (zero past its end).
@@ -350,25 +326,26 @@ __device__ __forceinline__ void block_store(const EncDst &d, bool sinks, uint32_
 
 // One lane per 1x16 block along the (head, dim) axis; blockIdx.y = 0: keys
 // (K_s = RN(K - mu)), 1: values.  The first two blocks of each lane are
-// loaded before the prologue, which reduces the key / value amax partials,
-// derives both tensor scales (workgroup (0,0) stores the decode scales into
-// the slot and the sink copies) and builds the (S, r) table of the
-// workgroup's tensor; afterwards each lane keeps two blocks in flight, with
-// the loop unrolled three times so the three block registers rotate without
-// copies.  Loads and stores are raw buffer accesses with 32-bit offsets:
-// a block past the end loads as zero and its stores are dropped by the
-// range check (also how only the blocks below the sink length reach the
-// sink copies).  When the grid stride is a multiple of the blocks per token
-// (MU_FIXED) every block of a lane starts at the same channel, and the lane
-// holds its 16 key means in registers; otherwise they are re-read per block.
+// loaded before the prologue, which takes the key (or value) amax as the
+// maximum of the channel groups' (or *v_amax_in), derives the tensor scale
+// (workgroup 0 stores the decode scale into the slot and the sink copies)
+// and builds the (S, r) table of the workgroup's tensor; afterwards each
+// lane keeps two blocks in flight, with the loop unrolled three times so
+// the three block registers rotate without copies.  Loads and stores are
+// raw buffer accesses with 32-bit offsets: a block past the end loads as
+// zero and its stores are dropped by the range check (also how only the
+// blocks below the sink length reach the sink copies).  When the grid
+// stride is a multiple of the blocks per token (MU_FIXED) every block of a
+// lane starts at the same channel, and the lane holds its 16 key means in
+// registers; otherwise they are re-read per block.
 template <bool FOUR_OVER_SIX, bool MU_FIXED>
 __global__ __launch_bounds__(256) void kv_encode_kernel(
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, int64_t nblk, int64_t HD,
-    const float *__restrict__ kpart, int nk, const float *__restrict__ vpart, int nv,
-    KvRegion slot, KvRegion gsink, KvRegion ssink, int64_t g_blk, int64_t s_blk) {
+    const float *__restrict__ gamax, const float *__restrict__ gvmax, int gy,
+    const float *__restrict__ v_amax_in, KvRegion slot, KvRegion gsink, KvRegion ssink,
+    int64_t g_blk, int64_t s_blk) {
     __shared__ f32x2 lut[128];
-    __shared__ float red[2][4];
-    __shared__ float sh[4];
+    __shared__ float sh[2];
     const int which = blockIdx.y;  // 0: keys, 1: values
     // nblk * 32 = T * HD * 2 < 2^32 bytes; block offsets are clamped to the
     // end so that they never wrap
@@ -388,42 +365,24 @@ __global__ __launch_bounds__(256) void kv_encode_kernel(
         load_raw16(slot.mu + ch0, m);
         unpack16(m, mu);
     }
-    float ak = 0.0f, av = 0.0f;
-    for (int i = threadIdx.x; i < nk; i += blockDim.x) ak = fmaxf(ak, kpart[i]);
-    for (int i = threadIdx.x; i < nv; i += blockDim.x) av = fmaxf(av, vpart[i]);
-    ak = wave_max(ak);
-    av = wave_max(av);
-    if ((threadIdx.x & 63) == 0) {
-        red[0][threadIdx.x >> 6] = ak;
-        red[1][threadIdx.x >> 6] = av;
-    }
-    __syncthreads();
     if (threadIdx.x == 0) {
-        const float a0 = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-        const float a1 = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
-        float e0, d0, e1, d1;
-        tensor_scales(a0, e0, d0);
-        tensor_scales(a1, e1, d1);
-        sh[0] = e0;
-        sh[1] = d0;
-        sh[2] = e1;
-        sh[3] = d1;
-        if (blockIdx.x == 0 && blockIdx.y == 0) {
-            slot.sd[0] = d0;
-            slot.sd[1] = d1;
-            if (g_blk > 0) {
-                gsink.sd[0] = d0;
-                gsink.sd[1] = d1;
-            }
-            if (s_blk > 0) {
-                ssink.sd[0] = d0;
-                ssink.sd[1] = d1;
-            }
+        const float *g = which ? gvmax : gamax;
+        float a = 0.0f;
+        for (int i = 0; i < gy; ++i) a = fmaxf(a, g[i]);
+        if (which == 1 && v_amax_in) a = *v_amax_in;
+        float e, d;
+        tensor_scales(a, e, d);
+        sh[0] = e;
+        sh[1] = d;
+        if (blockIdx.x == 0) {
+            slot.sd[which] = d;
+            if (g_blk > 0) gsink.sd[which] = d;
+            if (s_blk > 0) ssink.sd[which] = d;
         }
     }
     __syncthreads();
-    const float s_enc = sh[2 * which];
-    const float s_dec = sh[2 * which + 1];
+    const float s_enc = sh[0];
+    const float s_dec = sh[1];
     for (int c = threadIdx.x; c < 128; c += blockDim.x) lut[c] = scale_entry((uint32_t)c, s_dec);
     __syncthreads();
     EncDst d;
@@ -472,15 +431,23 @@ __global__ __launch_bounds__(256) void kv_encode_kernel(
 }
 
 hipError_t launch_kv_store(const KvStoreArgs &a, hipStream_t s) {
-    const KvDims d = kv_dims(a.T, a.HD);
-    KvWs w = carve_ws(a.ws, a.T, a.HD);
-    NVFP4_LAUNCH("kv_stats", kv_stats_kernel, dim3((unsigned)(d.nt64 * d.gy), 2), dim3(128), 0,
-                 s, a.K, a.V, a.T, a.HD, d.gy, w);
+    const int64_t nt64 = (a.T + kStatsTokens - 1) / kStatsTokens;
+    const int64_t gy = (a.HD + kGroupCh - 1) / kGroupCh;
+    KvWs w = carve_ws(a.ws, a.HD);
+    if (a.clear_ws) {
+        const int64_t n4 = kv_ws_zero_bytes(a.HD) / 4;
+        NVFP4_LAUNCH("kv_ws_clear", kv_ws_clear_kernel, dim3((unsigned)((n4 + 1023) / 1024)),
+                     dim3(256), 0, s, (uint32_t *)a.ws, n4);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const unsigned ny = a.v_amax_in ? 1u : 2u;
+    NVFP4_LAUNCH("kv_stats", kv_stats_kernel, dim3((unsigned)(nt64 * gy), ny), dim3(128), 0, s,
+                 a.K, a.V, a.T, a.HD, gy, w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    NVFP4_LAUNCH("kv_finalize", kv_finalize_kernel, dim3((unsigned)d.nfin), dim3(64), 0, s, w,
-                 d.nt64, d.n2, a.T, a.HD, a.slot.mu,
-                 a.g_tokens > 0 ? a.gsink.mu : (float *)nullptr,
+    NVFP4_LAUNCH("kv_finalize", kv_finalize_kernel, dim3((unsigned)gy), dim3(256), 0, s, w, a.T,
+                 a.HD, a.slot.mu, a.g_tokens > 0 ? a.gsink.mu : (float *)nullptr,
                  a.s_tokens > 0 ? a.ssink.mu : (float *)nullptr);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -507,11 +474,10 @@ hipError_t launch_kv_store(const KvStoreArgs &a, hipStream_t s) {
         fixed = true;
     }
     const int64_t g_blk = a.g_tokens * a.HD / 16, s_blk = a.s_tokens * a.HD / 16;
-    const int nk = (int)d.nfin, nv = (int)(d.nt64 * d.gy);
 #define NVFP4_ENC(F46, FIX)                                                                   \
     NVFP4_LAUNCH("kv_encode", (kv_encode_kernel<F46, FIX>), dim3((unsigned)g, 2), dim3(256), 0, \
-                 s, a.K, a.V, nblk, a.HD, (const float *)w.kpart, nk, (const float *)w.vpart, nv, \
-                 a.slot, a.gsink, a.ssink, g_blk, s_blk)
+                 s, a.K, a.V, nblk, a.HD, (const float *)w.gamax, (const float *)w.gvmax,       \
+                 (int)gy, a.v_amax_in, a.slot, a.gsink, a.ssink, g_blk, s_blk)
     if (a.search == 1) {
         if (fixed)
             NVFP4_ENC(true, true);

@@ -65,7 +65,9 @@ struct KvStoreArgs {
     KvRegion ssink;  // written when s_tokens > 0
     int64_t g_tokens;
     int64_t s_tokens;
-    void *ws;
+    const float *v_amax_in;  // nullptr: the stats pass takes the value amax itself
+    void *ws;                // accumulators zero unless clear_ws (see kv.hip)
+    bool clear_ws;           // zero them first (the first store of a ring)
 };
 size_t kv_store_ws_bytes(int64_t T, int64_t HD);
 hipError_t launch_kv_store(const KvStoreArgs &a, hipStream_t s);

@@ -34,7 +34,8 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.nvfp4_abi_version() == 1
+    assert L.nvfp4_abi_version() == 2
+    assert len(L.nvfp4_build_hash()) == 16
     for s in range(0, -7, -1):
         assert L.nvfp4_status_string(s)
     assert L.nvfp4_status_string(-99) == b"unknown status"
@@ -172,9 +173,12 @@ def test_ring_validation(L):
     assert L.nvfp4_kv_ring_init(C.byref(r), C.byref(bad), FAKE, 1 << 40) == -1
     r = make_ring(L)
     ws = L.nvfp4_kv_store_workspace_bytes(C.byref(c))
-    assert L.nvfp4_kv_store_chunk(C.byref(r), 1, FAKE, FAKE, FAKE, ws, None) == -5
-    assert L.nvfp4_kv_store_chunk(C.byref(r), 0, FAKE, FAKE, FAKE, ws - 1, None) == -4
-    assert L.nvfp4_kv_store_chunk(C.byref(r), 0, FAKE + 2, FAKE, FAKE, ws, None) == -2
+    assert L.nvfp4_kv_store_chunk(C.byref(r), 1, FAKE, FAKE, None, FAKE, ws, None) == -5
+    assert L.nvfp4_kv_store_chunk(C.byref(r), 0, FAKE, FAKE, None, FAKE, ws - 1, None) == -4
+    assert L.nvfp4_kv_store_chunk(C.byref(r), 0, FAKE + 2, FAKE, None, FAKE, ws, None) == -2
+    assert L.nvfp4_kv_store_chunk(C.byref(r), 0, FAKE, FAKE, FAKE + 2, FAKE, ws, None) == -2
+    # sums, max, min per channel; value max, key and value amax per 512-channel group
+    assert ws == 3072 * 16 + 3 * 256
     assert L.nvfp4_kv_begin_shot(C.byref(r), 3) == -5
     n = C.c_int64()
     assert L.nvfp4_kv_effective_tokens(C.byref(r), 1, C.byref(n)) == -5

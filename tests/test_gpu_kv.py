@@ -274,3 +274,34 @@ def test_gather_capacity_error(nv):
     with pytest.raises(nv.NVFP4Error):
         ring.store_chunk(5, Kg, Kg)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("factor", [1.0, 2.5, 0.5])
+def test_store_value_amax_from_producer(nv, orc, factor):
+    """The value tensor scale from a producer's amax (the statistics pass then
+    reads the keys only): with the true max|V| the ring holds the same bytes
+    as a plain store; with another amax the value codes, scales and decode
+    scale are the oracle's quantization of V with that amax (values beyond
+    it saturate), the keys unchanged."""
+    Lf, Fc, H, d = 40, 5, 3, 128
+    T, HD = Lf * Fc, H * d
+    print("case: store with producer value amax x", factor, flush=True)
+    cfg = nv.KVConfig(tokens_per_frame=Lf, frames_per_chunk=Fc, heads=H, head_dim=d,
+                      sink_frames_global=1, sink_frames_shot=1, window_chunks=2)
+    Kg, Vg, K, V = chunk_inputs(2400, 0, T, H, d)
+    vmax = np.float32(np.abs(V).max() * np.float32(factor))
+    ring = nv.KVRing(cfg)
+    ring.store_chunk(0, Kg, Vg, v_amax=torch.tensor([vmax], dtype=torch.float32, device="cuda"))
+    mem = ring_bytes(ring)
+    ref = orc.kv_encode_chunk(K, V)
+    vc, vs, sdv = orc.quantize(V, amax=float(vmax))
+    ref.update(vc=vc, vs=vs, sdv=sdv)
+    assert_region(region(mem, 0, T, HD), ref, T, HD)
+    assert_region(region(mem, ring.ring.gsink_offset, Lf, HD), ref, Lf, HD)
+    if factor == 1.0:  # the same bytes as a plain store, region by region
+        plain = nv.KVRing(cfg)
+        plain.store_chunk(0, Kg, Vg)
+        pm = ring_bytes(plain)
+        for off, n in ((0, T), (ring.ring.gsink_offset, Lf), (ring.ring.ssink_offset, Lf)):
+            got, want = region(mem, off, n, HD), region(pm, off, n, HD)
+            assert all(np.array_equal(got[k], want[k]) for k in got)
