@@ -350,6 +350,24 @@ int nvfp4_kv_store_chunk(nvfp4_kv_ring *ring, int64_t chunk_idx, const void *K_b
                          size_t workspace_bytes, void *stream);
 
 /*
+ * nvfp4_kv_store_chunk without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation).  Same arguments, checks and results as
+ * nvfp4_kv_store_chunk, bit for bit; the store's accumulators live in a
+ * fixed device array of the library instead (about 257 KB on every device
+ * the call runs on, kept until the process ends; located, and cleared by a
+ * fill kernel on `stream`, on the first call on each device).  Rejects
+ * heads * head_dim above NVFP4_KV_NOALLOC_MAX_CHANNELS with NVFP4_ENOSPC.
+ * Calls the library makes no allocation for.  Every call on one GPU shares
+ * that array: calls that overlap on one GPU (different streams, or host
+ * threads) race, whichever ring they store into; calls that follow one
+ * another in stream order do not.
+ */
+#define NVFP4_KV_NOALLOC_MAX_CHANNELS 16384
+int nvfp4_kv_store_chunk_noalloc(nvfp4_kv_ring *ring, int64_t chunk_idx, const void *K_bf16,
+                                 const void *V_bf16, const float *v_amax_in, void *stream);
+
+/*
  * Number of tokens in K_eff(step) (step must equal ring->next_chunk: the
  * step that generates chunk `step`).  K_eff(step) = (A_g u A_s u
  * [max(0, step-W)*T_c, step*T_c)) n [0, step*T_c).  Pure host.

@@ -93,6 +93,8 @@ _EXPORTS = {
     "nvfp4_kv_begin_shot": ([C.POINTER(CKvRing), C.c_int64], C.c_int),
     "nvfp4_kv_store_chunk": ([C.POINTER(CKvRing), C.c_int64, C.c_void_p, C.c_void_p,
                               C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p], C.c_int),
+    "nvfp4_kv_store_chunk_noalloc": ([C.POINTER(CKvRing), C.c_int64, C.c_void_p, C.c_void_p,
+                                      C.c_void_p, C.c_void_p], C.c_int),
     "nvfp4_kv_effective_tokens": ([C.POINTER(CKvRing), C.c_int64, C.POINTER(C.c_int64)],
                                   C.c_int),
     "nvfp4_gather_window": ([C.POINTER(CKvRing), C.c_int64, C.c_void_p, C.c_void_p, C.c_int64,
@@ -440,6 +442,19 @@ class KVRing:
                                           _dev(V, "V"), _amax_arg(v_amax, "v_amax"),
                                           C.c_void_p(self.ws.data_ptr()), self.ws.numel(),
                                           _stream(stream)))
+
+    def store_chunk_noalloc(self, chunk_idx: int, K: torch.Tensor, V: torch.Tensor,
+                            v_amax: torch.Tensor | None = None, stream=None):
+        """nvfp4_kv_store_chunk_noalloc: as store_chunk, with the library's
+        fixed device scratch instead of this ring's workspace."""
+        if K.dtype != torch.bfloat16 or V.dtype != torch.bfloat16:
+            raise ValueError("K and V must be bfloat16")
+        T, hd = self.cfg.chunk_tokens, self.cfg.heads * self.cfg.head_dim
+        if K.numel() != T * hd or V.numel() != T * hd:
+            raise ValueError(f"K and V must hold [{T}, {self.cfg.heads}, {self.cfg.head_dim}]")
+        _check(lib().nvfp4_kv_store_chunk_noalloc(C.byref(self.ring), chunk_idx, _dev(K, "K"),
+                                                  _dev(V, "V"), _amax_arg(v_amax, "v_amax"),
+                                                  _stream(stream)))
 
     def effective_tokens(self, step: int) -> int:
         n = C.c_int64()

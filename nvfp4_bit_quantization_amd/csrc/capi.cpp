@@ -448,23 +448,39 @@ int nvfp4_kv_begin_shot(nvfp4_kv_ring *ring, int64_t chunk_idx) {
     return ok();
 }
 
-int nvfp4_kv_store_chunk(nvfp4_kv_ring *ring, int64_t chunk_idx, const void *K_bf16,
-                         const void *V_bf16, const float *v_amax_in, void *workspace,
-                         size_t workspace_bytes, void *stream) {
+static_assert(NVFP4_KV_NOALLOC_MAX_CHANNELS == 16384, "allocation-free store limit");
+
+static int kv_store(nvfp4_kv_ring *ring, int64_t chunk_idx, const void *K_bf16,
+                    const void *V_bf16, const float *v_amax_in, void *workspace,
+                    size_t workspace_bytes, void *stream, bool noalloc) {
+    const char *who = noalloc ? "kv_store_chunk_noalloc" : "kv_store_chunk";
     int st = check_ring(ring);
     if (st) return st;
     if (chunk_idx != ring->next_chunk)
-        return fail(NVFP4_ESTATE, "kv_store_chunk: chunk %lld stored out of order (next %lld)",
+        return fail(NVFP4_ESTATE, "%s: chunk %lld stored out of order (next %lld)", who,
                     (long long)chunk_idx, (long long)ring->next_chunk);
-    if (!K_bf16 || !V_bf16) return fail(NVFP4_EINVAL, "kv_store_chunk: NULL K or V");
-    if (!aligned16(K_bf16) || !aligned16(V_bf16) || !aligned16(workspace))
-        return fail(NVFP4_EALIGN, "kv_store_chunk: K, V and workspace must be 16-byte aligned");
-    if ((uintptr_t)v_amax_in & 3u)
-        return fail(NVFP4_EALIGN, "kv_store_chunk: v_amax_in misaligned");
+    if (!K_bf16 || !V_bf16) return fail(NVFP4_EINVAL, "%s: NULL K or V", who);
+    if (!aligned16(K_bf16) || !aligned16(V_bf16))
+        return fail(NVFP4_EALIGN, "%s: K and V must be 16-byte aligned", who);
+    if ((uintptr_t)v_amax_in & 3u) return fail(NVFP4_EALIGN, "%s: v_amax_in misaligned", who);
     const size_t need = nvfp4_kv_store_workspace_bytes(&ring->cfg);
-    if (!workspace || workspace_bytes < need)
-        return fail(NVFP4_ENOSPC, "kv_store_chunk: workspace %zu < %zu bytes", workspace_bytes,
-                    need);
+    if (noalloc) {
+        if (ring->hd > nvfp4::kv_noalloc_max_hd())
+            return fail(NVFP4_ENOSPC,
+                        "%s: heads * head_dim = %lld exceeds the %lld channels its fixed scratch "
+                        "holds (use nvfp4_kv_store_chunk with a workspace)",
+                        who, (long long)ring->hd, (long long)nvfp4::kv_noalloc_max_hd());
+        hipError_t e = nvfp4::kv_noalloc_scratch(&workspace, &workspace_bytes, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_status(e, "kv_store_chunk_noalloc scratch");
+        if (workspace_bytes < need)
+            return fail(NVFP4_ENOSPC, "%s: scratch %zu < %zu bytes", who, workspace_bytes, need);
+    } else {
+        if (!aligned16(workspace))
+            return fail(NVFP4_EALIGN, "%s: workspace must be 16-byte aligned", who);
+        if (!workspace || workspace_bytes < need)
+            return fail(NVFP4_ENOSPC, "%s: workspace %zu < %zu bytes", who, workspace_bytes,
+                        need);
+    }
     const nvfp4_kv_config &c = ring->cfg;
     const int64_t T = ring->chunk_tokens, hd = ring->hd;
     const int64_t gtok = (int64_t)c.sink_frames_global * c.tokens_per_frame;
@@ -485,9 +501,22 @@ int nvfp4_kv_store_chunk(nvfp4_kv_ring *ring, int64_t chunk_idx, const void *K_b
     a.ws = workspace;
     a.clear_ws = (chunk_idx == 0);
     hipError_t e = nvfp4::launch_kv_store(a, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_status(e, "kv_store_chunk launch");
+    if (e != hipSuccess) return hip_status(e, noalloc ? "kv_store_chunk_noalloc launch"
+                                                      : "kv_store_chunk launch");
     ring->next_chunk = chunk_idx + 1;
     return ok();
+}
+
+int nvfp4_kv_store_chunk(nvfp4_kv_ring *ring, int64_t chunk_idx, const void *K_bf16,
+                         const void *V_bf16, const float *v_amax_in, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    return kv_store(ring, chunk_idx, K_bf16, V_bf16, v_amax_in, workspace, workspace_bytes,
+                    stream, false);
+}
+
+int nvfp4_kv_store_chunk_noalloc(nvfp4_kv_ring *ring, int64_t chunk_idx, const void *K_bf16,
+                                 const void *V_bf16, const float *v_amax_in, void *stream) {
+    return kv_store(ring, chunk_idx, K_bf16, V_bf16, v_amax_in, nullptr, 0, stream, true);
 }
 
 int nvfp4_kv_effective_tokens(const nvfp4_kv_ring *ring, int64_t step, int64_t *n_tokens) {

@@ -29,6 +29,8 @@
 // Gather = one launch: one workgroup-iteration per kGatherTok output tokens,
 // one lane per 16-element block; each token's segment (ring slot or sink
 // copy) is found from scalars (sink lengths, window start, W).
+#include <mutex>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -428,6 +430,49 @@ __global__ __launch_bounds__(256) void kv_encode_kernel(
         rb = block_load(xr, off(b + 4 * stride));
         encode(rc, b + 2 * stride);
     }
+}
+
+// ---------------------------------------------------------------------------
+// Store scratch without allocation: the store's workspace as a file-scope
+// device array (each device the library runs on holds one until the process
+// ends).  Its host-side name is only a stand-in: the device address comes
+// from hipGetSymbolAddress, once per device, with that device current.
+// ---------------------------------------------------------------------------
+
+constexpr int64_t kNoallocMaxHD = 16384;
+constexpr size_t kNoallocScratchBytes =
+    (size_t)(((kNoallocMaxHD * 8 + 255) & ~255) + 2 * ((kNoallocMaxHD * 4 + 255) & ~255) +
+             3 * 256);
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+int64_t kv_noalloc_max_hd() { return kNoallocMaxHD; }
+static_assert(kNoallocMaxHD == 16384, "allocation-free store limit (nvfp4.h)");
+
+hipError_t kv_noalloc_scratch(void **ptr, size_t *bytes, hipStream_t s) {
+    static std::mutex mu;
+    static void *dev_ptr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!dev_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        // zero the accumulators once, ahead of the first store on the
+        // caller's stream (a fill kernel, not a memset node; the array also
+        // starts zero-initialised)
+        const int64_t n4 = (int64_t)kNoallocScratchBytes / 4;
+        hipLaunchKernelGGL(kv_ws_clear_kernel, dim3((unsigned)((n4 + 1023) / 1024)), dim3(256), 0,
+                           s, (uint32_t *)p, n4);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        dev_ptr[dev] = p;
+    }
+    *ptr = dev_ptr[dev];
+    *bytes = kNoallocScratchBytes;
+    return hipSuccess;
 }
 
 hipError_t launch_kv_store(const KvStoreArgs &a, hipStream_t s) {

@@ -71,6 +71,13 @@ struct KvStoreArgs {
 };
 size_t kv_store_ws_bytes(int64_t T, int64_t HD);
 hipError_t launch_kv_store(const KvStoreArgs &a, hipStream_t s);
+constexpr int kMaxDevices = 64;
+// Largest heads * head_dim the allocation-free store takes.
+int64_t kv_noalloc_max_hd();
+// Device address and size of the allocation-free store's scratch on the
+// current device (looked up, and zeroed on stream s, on the first call per
+// device).
+hipError_t kv_noalloc_scratch(void **ptr, size_t *bytes, hipStream_t s);
 
 // Gather plan of K_eff(t): n_g tokens from the global-sink copy, then n_s
 // tokens from the shot-sink copy (both only when outside the window), then
