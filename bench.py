@@ -438,8 +438,18 @@ def run_quant_act(nv, args, dev, M=7040, K=3072):
     ms, wall, med = time_steps(step, args.steps, args.warmup, per_step=True)
     kt = kernel_times(nv, step, max(5, args.steps // 5), 0)
     alg = M * K * 2 + M * K // 2 + M * K // 16 + 4
+    # and back: dequantize each set to bf16 (rotated outputs)
+    Ys = [torch.empty((M, K), dtype=torch.bfloat16, device=dev) for _ in range(args.sets)]
+
+    def dstep(i):
+        j = i % args.sets
+        nv.dequantize(outs[j], out=Ys[j])
+
+    dms, _, dmed = time_steps(dstep, args.steps, args.warmup, per_step=True)
+    dkt = kernel_times(nv, dstep, max(5, args.steps // 5), 0)
     return {"ms": ms, "wall_ms": wall, "median_ms": med, "gbs": alg / ms / 1e6, "alg_bytes": alg,
-            "kernels": kt}
+            "kernels": kt, "dequant_ms": dms, "dequant_median_ms": dmed,
+            "dequant_gbs": alg / dms / 1e6, "dequant_kernel_ms": dkt["dequant"][1]}
 
 
 def run_ffn(nv, args, dev):
@@ -826,6 +836,11 @@ def main():
             "alg_bytes": q["alg_bytes"],
             "kernels_us": {k: round(v[1] * 1e3, 2) for k, v in q["kernels"].items()},
             "cache": f"cold: {max(4, args.sets)} rotated input and output sets (4 x 43 MB bf16 in)"}
+        sec["dequantize_act_7040x3072_to_bf16_cold"] = {
+            "GB/s": round(q["dequant_gbs"], 1), "frac_hbm_peak": round(q["dequant_gbs"] / HBM_PEAK_GBS, 4),
+            "us": round(q["dequant_ms"] * 1e3, 2), "median_us": round(q["dequant_median_ms"] * 1e3, 2),
+            "kernel_us": round(q["dequant_kernel_ms"] * 1e3, 2), "alg_bytes": q["alg_bytes"],
+            "cache": f"cold: {max(4, args.sets)} rotated sets"}
         w = run_wgrad(nv, argparse.Namespace(steps=10, warmup=3, sets=args.sets), dev)
         sec["wgrad_3072x3072x7040_1d_operands"] = w
         lo = run_lora(nv, argparse.Namespace(steps=20, warmup=5, sets=args.sets), dev)

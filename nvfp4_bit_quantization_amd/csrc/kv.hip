@@ -26,9 +26,8 @@
 //                amaxes, then the 1-D 4/6 encoder over K_s = RN(K - mu) and
 //                V, writing the ring slot and, for sink chunks, the sink copy
 //                in the same pass
-// Gather = one launch: one workgroup-iteration per kGatherTok output tokens,
-// one lane per 16-element block; each token's segment (ring slot or sink
-// copy) is found from scalars (sink lengths, window start, W).
+// Gather = one launch: workgroups take runs of tokens of one segment (ring
+// slot or sink copy) of the effective set, a lane per half block.
 #include <mutex>
 
 #include "device.hpp"
@@ -542,96 +541,66 @@ hipError_t launch_kv_store(const KvStoreArgs &a, hipStream_t s) {
 // Gather-dequantize of K_eff(t)
 // ---------------------------------------------------------------------------
 
-// Output order: [global-sink tokens outside the window][shot-sink tokens
-// outside the window][window chunks c_lo .. c_lo + nwin - 1]; sinks lie below
-// the window in token order, so this is ascending token order.
-__device__ __forceinline__ void gather_region(const GatherArgs &a, int64_t tok, KvRegion &r,
-                                              int64_t &st) {
-    if (tok < a.n_g) {
-        r = a.gsink;
-        st = tok;
-    } else if (tok < a.n_g + a.n_s) {
-        r = a.ssink;
-        st = tok - a.n_g;
-    } else {
-        const int64_t w = tok - a.n_g - a.n_s;
-        const int64_t q = w / a.Tc;
-        const int64_t off = ((a.c_lo + q) % a.W) * a.slot_bytes;
-        r.kc = a.slot0.kc + off;
-        r.ks = a.slot0.ks + off;
-        r.vc = a.slot0.vc + off;
-        r.vs = a.slot0.vs + off;
-        r.mu = (float *)((uint8_t *)a.slot0.mu + off);
-        r.sd = (float *)((uint8_t *)a.slot0.sd + off);
-        st = w - q * a.Tc;
-    }
-}
-
-// Each workgroup-iteration covers kGatherTok consecutive output tokens; lane
-// j expands block j (16 elements) of K and V of each of them, with the loads
-// of all the tokens issued before any of them is expanded.
+// Each workgroup takes tpw consecutive tokens of one segment (found once,
+// from the plan's first-workgroup table), so every token's region, key mean
+// and decode scales are the workgroup's.  Lane i expands half-block i of K
+// and V of each token (elements 8 i .. 8 i + 7: block i >> 1's scale and
+// one dword of its codes), its 8 key means held in registers, with the
+// loads of four tokens issued before any of them is expanded; each store
+// instruction of a wave then writes 1 KB contiguous (a lane per whole block
+// wrote 32 bytes at a 32-byte stride in two instructions: 141 against
+// 113 us for the 33,440-token set of the 64 s ring).  Output rows follow the
+// segments: ascending token order.
 constexpr int kGatherTok = 4;
 
-__global__ __launch_bounds__(256) void kv_gather_kernel(GatherArgs a) {
+__global__ __launch_bounds__(512) void kv_gather_kernel(GatherArgs a) {
+    int s = 0;
+    while (s + 1 < a.nseg && (int)blockIdx.x >= a.wg0[s + 1]) ++s;
+    const KvSeg &g = a.seg[s];
+    const int64_t t_begin = (int64_t)((int)blockIdx.x - a.wg0[s]) * a.tpw;
+    const int64_t t_end = t_begin + a.tpw < g.n ? t_begin + a.tpw : g.n;
     const int64_t NB = a.HD >> 4;  // blocks per token
-    for (int64_t tok0 = (int64_t)blockIdx.x * kGatherTok; tok0 < a.n_tokens;
-         tok0 += (int64_t)gridDim.x * kGatherTok) {
-        for (int64_t j = threadIdx.x; j < NB; j += blockDim.x) {
-            uint2 qk[kGatherTok], qv[kGatherTok];
-            uint32_t sk[kGatherTok], sv[kGatherTok];
-            const float *mup[kGatherTok];
-            float sdk[kGatherTok], sdv[kGatherTok];
+    const float sdk = g.sd[0], sdv = g.sd[1];
+    const uint32_t *kc = (const uint32_t *)g.kc, *vc = (const uint32_t *)g.vc;
+    uint16_t *Ko = a.Kout + a.out0[s] * a.HD, *Vo = a.Vout + a.out0[s] * a.HD;
+    for (int64_t i = threadIdx.x; i < 2 * NB; i += blockDim.x) {
+        const int64_t j = i >> 1;
+        float mu[8];
+        load8(g.mu + i * 8, mu);
+        for (int64_t t0 = t_begin; t0 < t_end; t0 += kGatherTok) {
+            uint32_t qk[kGatherTok], qv[kGatherTok], sk[kGatherTok], sv[kGatherTok];
 #pragma unroll
             for (int k = 0; k < kGatherTok; ++k) {
-                const int64_t tok = tok0 + k < a.n_tokens ? tok0 + k : a.n_tokens - 1;
-                KvRegion r;
-                int64_t st;
-                gather_region(a, tok, r, st);
-                qk[k] = ((const uint2 *)r.kc)[st * NB + j];
-                qv[k] = ((const uint2 *)r.vc)[st * NB + j];
-                sk[k] = r.ks[st * NB + j];
-                sv[k] = r.vs[st * NB + j];
-                sdk[k] = r.sd[0];
-                sdv[k] = r.sd[1];
-                mup[k] = r.mu + j * 16;
+                const int64_t t = t0 + k < t_end ? t0 + k : t_end - 1;
+                qk[k] = kc[t * 2 * NB + i];
+                qv[k] = vc[t * 2 * NB + i];
+                sk[k] = g.ks[t * NB + j];
+                sv[k] = g.vs[t * NB + j];
             }
 #pragma unroll
             for (int k = 0; k < kGatherTok; ++k) {
-                const int64_t tok = tok0 + k;
-                if (tok >= a.n_tokens) break;
-                Raw16F32 m;
-                load_raw16(mup[k], m);
-                float mu[16];
-                unpack16(m, mu);
-                const float Sk = e4m3_value(sk[k]) * sdk[k];
-                const float Sv = e4m3_value(sv[k]) * sdv[k];
-                uint16_t *ko = a.Kout + tok * a.HD + j * 16;
-                uint16_t *vo = a.Vout + tok * a.HD + j * 16;
+                const int64_t t = t0 + k;
+                if (t >= t_end) break;
+                const float Sk = e4m3_value(sk[k]) * sdk;
+                const float Sv = e4m3_value(sv[k]) * sdv;
                 float y[8];
-                dequant8(qk[k].x, Sk, y);
+                dequant8(qk[k], Sk, y);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) y[i] = y[i] + mu[i];
-                store8(ko, y);
-                dequant8(qk[k].y, Sk, y);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) y[i] = y[i] + mu[8 + i];
-                store8(ko + 8, y);
-                dequant8(qv[k].x, Sv, y);
-                store8(vo, y);
-                dequant8(qv[k].y, Sv, y);
-                store8(vo + 8, y);
+                for (int e = 0; e < 8; ++e) y[e] = y[e] + mu[e];
+                store8(Ko + t * a.HD + i * 8, y);
+                dequant8(qv[k], Sv, y);
+                store8(Vo + t * a.HD + i * 8, y);
             }
         }
     }
 }
 
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s) {
-    if (a.n_tokens == 0) return hipSuccess;
+    const int g = a.wg0[a.nseg];
+    if (g == 0) return hipSuccess;
     const int64_t NB = a.HD >> 4;
-    int64_t bs = ((NB + 63) / 64) * 64;
-    if (bs > 256) bs = 256;
-    int64_t g = (a.n_tokens + kGatherTok - 1) / kGatherTok;
-    if (g > 2048) g = 2048;
+    int64_t bs = ((2 * NB + 63) / 64) * 64;
+    if (bs > 512) bs = 512;
     NVFP4_LAUNCH("kv_gather", kv_gather_kernel, dim3((unsigned)g), dim3((unsigned)bs), 0, s, a);
     return hipGetLastError();
 }

@@ -79,20 +79,27 @@ int64_t kv_noalloc_max_hd();
 // device).
 hipError_t kv_noalloc_scratch(void **ptr, size_t *bytes, hipStream_t s);
 
-// Gather plan of K_eff(t): n_g tokens from the global-sink copy, then n_s
-// tokens from the shot-sink copy (both only when outside the window), then
-// the window chunks c_lo, c_lo+1, ... (chunk c in slot c mod W).
+// A run of consecutive stored tokens of one ring region (a chunk slot or a
+// sink copy): one key mean, one pair of decode scales.  K_eff(t) is up to
+// 2 + W such segments in ascending token order (global sink part, shot sink
+// part, window chunks).
+constexpr int kMaxSeg = 2 + 16;
+struct KvSeg {
+    const uint8_t *kc, *ks, *vc, *vs;  // codes / scales of the segment's first token
+    const float *mu;                   // [HD] key mean of the region
+    const float *sd;                   // [2] decode scales (K_s, V)
+    int64_t n;                         // tokens
+};
+
+// Gather plan: workgroups [wg0[s], wg0[s + 1]) take segment s, tpw tokens
+// each (the last one fewer); segment s's tokens go to output rows
+// out0[s] .. out0[s] + n - 1.
 struct GatherArgs {
-    KvRegion gsink;
-    KvRegion ssink;
-    KvRegion slot0;      // slot 0; slot k is slot0 + k * slot_bytes
-    int64_t slot_bytes;
-    int64_t n_g;
-    int64_t n_s;
-    int64_t c_lo;
-    int64_t Tc;
-    int64_t W;
-    int64_t n_tokens;
+    KvSeg seg[kMaxSeg];
+    int32_t wg0[kMaxSeg + 1];
+    int64_t out0[kMaxSeg];
+    int32_t nseg;
+    int32_t tpw;
     int64_t HD;
     uint16_t *Kout;
     uint16_t *Vout;
@@ -103,13 +110,8 @@ hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
 // Attention over K_eff(t) read packed from the ring: the effective set as
 // up to 2 + W segments, each a run of consecutive tokens of one region (one
 // key mean, one pair of decode scales), in ascending token order.
-constexpr int kAttnMaxSeg = 2 + 16;
-struct AttnSeg {
-    const uint8_t *kc, *ks, *vc, *vs;  // codes / scales of the segment's first token
-    const float *mu;                   // [HD] key mean of the region
-    const float *sd;                   // [2] decode scales (K_s, V)
-    int64_t n;                         // tokens
-};
+constexpr int kAttnMaxSeg = kMaxSeg;
+typedef KvSeg AttnSeg;
 struct AttnArgs {
     AttnSeg seg[kAttnMaxSeg];
     int32_t tile0[kAttnMaxSeg + 1];  // first 64-key tile of each segment, tile0[nseg] = total

@@ -14,7 +14,7 @@
 //                    candidates in registers), two blocks in flight, raw
 //                    buffer loads and stores
 //   encode2d_kernel  32 lanes own a 16x16 tile (lane pair = tile row)
-//   dequant_kernel   8 elements per lane, 16-byte stores
+//   dequant_kernel   16 output bytes per lane (one 16-byte store)
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -274,28 +274,37 @@ __global__ __launch_bounds__(256) void encode2d_kernel(
 // Dequantize
 // ---------------------------------------------------------------------------
 
+// One lane per 16 output bytes (8 bf16 or 4 fp32 elements, inside one
+// block): its codes (a dword or a half word), the block's scale byte, one
+// 16-byte store, so each store instruction of a wave writes 1 KB
+// contiguous.
 template <typename TOUT, bool TWO_D>
-__global__ __launch_bounds__(256) void dequant_kernel(const uint2 *__restrict__ codes,
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict__ codes,
                                                       const uint8_t *__restrict__ scales,
                                                       const float *__restrict__ s_dec_p,
-                                                      int64_t nblk, int64_t cols,
+                                                      int64_t nvec, int64_t cols,
                                                       TOUT *__restrict__ y) {
+    constexpr int E = 16 / (int)sizeof(TOUT);  // elements per lane
     const float s_dec = *s_dec_p;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const int64_t tcols = cols >> 4;
-    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += stride) {
+    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += stride) {
+        const int64_t e0 = v * E, b = e0 >> 4;
         int64_t si = b;
         if (TWO_D) {
             const int64_t row = b / tcols, cb = b - row * tcols;
             si = (row >> 4) * tcols + cb;
         }
-        const uint2 q = codes[b];
         const float S = e4m3_value(scales[si]) * s_dec;
-        float v[8];
-        dequant8(q.x, S, v);
-        store8(y + b * 16, v);
-        dequant8(q.y, S, v);
-        store8(y + b * 16 + 8, v);
+        float out[8];
+        if (E == 8) {
+            dequant8(((const uint32_t *)codes)[v], S, out);
+            store8((uint16_t *)y + e0, out);
+        } else {
+            const uint32_t q = ((const uint16_t *)codes)[v];
+            f32x2 w0 = e2m1_unpack2<0>(q), w1 = e2m1_unpack2<1>(q);
+            *(f32x4 *)((float *)y + e0) = f32x4{w0.x * S, w0.y * S, w1.x * S, w1.y * S};
+        }
     }
 }
 
@@ -408,12 +417,11 @@ hipError_t launch_quantize_rht(const void *x, int dtype, int64_t rows, int64_t c
 hipError_t launch_dequant(const uint8_t *codes, const uint8_t *scales, const float *s_dec,
                           int64_t rows, int64_t cols, int layout, void *y, int ydtype,
                           hipStream_t s) {
-    const int64_t nblk = rows * cols / 16;
-    const int g = grid_for(nblk, 256 * 2, 8192);
-    const uint2 *c64 = (const uint2 *)codes;
-#define LD(T, TWO)                                                                     \
-    NVFP4_LAUNCH("dequant", (dequant_kernel<T, TWO>), dim3(g), dim3(256), 0, s, c64, scales, \
-                 s_dec, nblk, cols, (T *)y)
+    const int64_t nvec = rows * cols * (ydtype == kF32 ? 4 : 2) / 16;
+    const int g = grid_for(nvec, 256 * 4, 8192);
+#define LD(T, TWO)                                                                      \
+    NVFP4_LAUNCH("dequant", (dequant_kernel<T, TWO>), dim3(g), dim3(256), 0, s, codes, scales, \
+                 s_dec, nvec, cols, (T *)y)
     if (ydtype == kF32) {
         if (layout) LD(float, true); else LD(float, false);
     } else {

@@ -26,9 +26,10 @@ def bf16(bits, shape):
 
 
 def written_regions(ring, n_slots):
-    """Bytes of the ring regions the stores so far have written: the first
-    n_slots chunk slots and both sink regions (their packed data, mu and
-    decode scales)."""
+    """The arrays the stores so far have written, each at its exact length
+    (the 256-byte alignment padding between them is never written): of the
+    first n_slots chunk slots and both sink regions, K and V codes and
+    scales, mu and the two decode scales."""
     torch.cuda.synchronize()
     mem = ring.mem.cpu().numpy()[ring._base - ring.mem.data_ptr():]
     r = ring.ring
@@ -37,12 +38,17 @@ def written_regions(ring, n_slots):
     a = lambda n: (n + 255) // 256 * 256
 
     def reg(off, ntok):
-        n = 2 * (a(ntok * hd // 2) + a(ntok * hd // 16)) + a(hd * 4) + 8
-        return mem[off:off + n]
+        out, o = [], off
+        for n in (ntok * hd // 2, ntok * hd // 16, ntok * hd // 2, ntok * hd // 16, hd * 4, 8):
+            out.append(mem[o:o + n])
+            o += a(n)
+        return out
 
-    out = [reg(k * r.slot_bytes, T) for k in range(n_slots)]
-    out.append(reg(r.gsink_offset, cfg.sink_frames_global * cfg.tokens_per_frame))
-    out.append(reg(r.ssink_offset, cfg.sink_frames_shot * cfg.tokens_per_frame))
+    out = []
+    for k in range(n_slots):
+        out += reg(k * r.slot_bytes, T)
+    out += reg(r.gsink_offset, cfg.sink_frames_global * cfg.tokens_per_frame)
+    out += reg(r.ssink_offset, cfg.sink_frames_shot * cfg.tokens_per_frame)
     return out
 
 
