@@ -311,9 +311,9 @@ struct LoraArgs {
     float scale;
 };
 
-// Per-wave LDS of the fused epilogue: the wave's 128 x 96 tile of bf16(Y)
-// (row-major, 192 bytes a row), then the (S, 1/S) table of the 128
-// non-negative scale codes for the tensor's s_dec.
+// Per-wave LDS of the bf16 and fused-encode epilogues: the wave's 128 x 96
+// tile of bf16(Y) (row-major, 192 bytes a row), then (fused encode) the
+// (S, 1/S) table of the 128 non-negative scale codes for the tensor's s_dec.
 constexpr int kQRowBytes = WN * 2;
 constexpr int kQTileBytes = WM * kQRowBytes;           // 24576
 constexpr int kQLutOff = kQTileBytes;
@@ -384,8 +384,9 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
         }
         // no load into LDS is still in flight when the wave leaves
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        // the fused encode reuses the stages: every wave is past its last read
-        if (QUANT) __syncthreads();
+        // the fused encode and the bf16 epilogue reuse the stages: every wave
+        // is past its last read
+        if (QUANT || OUT_BF16) __syncthreads();
     } else if (active) {
         FragPtr pa[FM], pb[FN];
 #pragma unroll
@@ -462,7 +463,7 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
                     const int64_t row = rbase + (e >> 2) * 8 + (e & 3);
                     float v = scale * acc[i][j][e];
                     if (LORA) v = __builtin_fmaf(la.scale, lo[ii][j][e], v);
-                    if (QUANT) {
+                    if (QUANT || (OUT_BF16 && KFAST)) {
                         const __bf16 b = (__bf16)v;
                         if (row < M && col < N) amax = fmaxf(amax, fabsf((float)b));
                         const int rl = i * 32 + h * 4 + (e >> 2) * 8 + (e & 3);
@@ -479,6 +480,22 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
                     }
                 }
             }
+    }
+    if (!QUANT && OUT_BF16 && KFAST) {
+        // bf16 Y: the wave's tile went to its LDS region (row-major, 192 bytes
+        // a row, so 16-byte piece c of the tile sits at byte 16 c); back in
+        // 16-byte row pieces, one 16-byte store each (lane-strided 2-byte
+        // stores straight from the accumulators took 141 against 131 us on
+        // 7040 x 3072 x 3072).  Only this wave touches its region.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        constexpr int kPieces = WN / 8;  // 12 a row
+#pragma unroll 4
+        for (int k = 0; k < WM * kPieces / 64; ++k) {
+            const int c = lane + 64 * k, rl = c / kPieces, cc = c - rl * kPieces;
+            const int64_t row = mw + rl, col = nw + cc * 8;
+            const u32x4 v = *(const u32x4 *)(qw + c * 16);
+            if (row < M && col < N) *(u32x4 *)((__bf16 *)yv + row * N + col) = v;
+        }
     }
     if (QUANT) {
         // 1x16 blocks of the wave's tile, 12 per lane: bf16 values back from
