@@ -12,7 +12,7 @@
 // uses micro-block scaling with the Four Over Six selection.
 //
 // Store = three launches:
-//   kv_stats     two waves per (64-token node, 512 channels): per-channel key
+//   kv_stats     four waves per (256-token node, 512 channels): per-channel key
 //                sums in double, key max / min and the value |max| over the
 //                node, added into the workspace with device-scope atomics
 //                (the sums are exact on the key-mean domain, so their order
@@ -35,9 +35,11 @@
 
 namespace nvfp4 {
 
-constexpr int kStatsTokens = 64;      // tokens per stats unit (two waves of 32)
+constexpr int kHalf = 32;             // tokens per stats batch (all its loads in flight at once)
+constexpr int kStatsWaves = 4;        // waves per stats workgroup
+constexpr int kStatsBatches = 2;      // batches per stats wave
+constexpr int kStatsTokens = kHalf * kStatsBatches * kStatsWaves;  // tokens per stats unit
 constexpr int kGroupCh = 512;         // channels per stats unit (64 lanes x 8)
-constexpr int kHalf = kStatsTokens / 2;  // tokens per stats wave
 constexpr int64_t kEncodeGrid = 4096; // encode workgroups per tensor (upper bound)
 constexpr int64_t kEncodeBlocks = 6;  // target blocks per encode lane (measured: 6 over ~10)
 
@@ -139,35 +141,37 @@ __device__ __forceinline__ float stats_value_token(const u32x4 &r, float m) {
     return m;
 }
 
-// Workgroup = 2 waves = one unit (64-token node p, 512-channel group y);
+// Workgroup = 4 waves = one unit (256-token node p, 512-channel group y);
 // blockIdx.y selects keys (0) or values (1; absent when the caller supplies
-// the value amax).  Wave h takes tokens 64 p + 32 h .. +31; lane l owns
-// channels 512 y + 8 l .. +7 (one 16-byte load per token), and all 32 loads
-// of a wave are issued before any is used; the last, partial node reads
-// token by token up to T.  Keys: per-channel double sums, max and min over
-// the wave's tokens; both waves put theirs in LDS and the workgroup adds
-// the unit's 512 channels to the workspace with atomics, thread t taking
-// channels t + 128 j so that one atomic instruction covers consecutive
-// addresses (atomic add of the sums, atomic max of the order-preserving
-// bits of max and of -min; measured: lane-strided atomics cost 30 us a
-// chunk, consecutive ones 2 us).  Values: the unit's |max|, one atomic max
-// into its channel group's word.  Each double sum and every partial sum
-// the atomics form is exact on the key-mean domain (every partial sum of a
-// channel's keys is a multiple of the channel's smallest key unit below
-// 2^53 of them), so mu does not depend on the order in which units arrive.
-// (Measured alternatives to the kv_finalize launch: finalizing in the
-// last-arriving workgroup of each group, found by a ticket counter, 9-10 us
-// slower, since every workgroup then waits for its atomics to be performed
-// before it can take a ticket and retire; finalizing in every kv_encode
-// workgroup's prologue, ~5 us slower, since each key workgroup reads all
-// the channels' statistics and divides for every channel.)
-__global__ __launch_bounds__(128) void kv_stats_kernel(const uint16_t *__restrict__ K,
-                                                       const uint16_t *__restrict__ V, int64_t T,
-                                                       int64_t HD, int64_t gy, KvWs w) {
-    __shared__ double sp[2][8][64];
-    __shared__ float sx[2][8][64];
-    __shared__ float sn[2][8][64];
-    __shared__ float red[2];
+// the value amax).  Wave h takes tokens 256 p + 64 h .. +63 in two batches
+// of 32; lane l owns channels 512 y + 8 l .. +7 (one 16-byte load per
+// token), and all 32 loads of a batch are issued before any is used; a
+// partial batch (past T) reads token by token.  Keys: per-channel double
+// sums, max and min over the wave's tokens; the waves put theirs in LDS and
+// the workgroup adds the unit's 512 channels to the workspace with atomics,
+// thread t taking channels t and t + 256 so that one atomic instruction
+// covers consecutive addresses (atomic add of the sums, atomic max of the
+// order-preserving bits of max and of -min).  Values: the unit's |max|, one
+// atomic max into its channel group's word.  The device-scope atomics bound
+// this kernel (774K of them take about 10 us on their own, measured), so a
+// unit spans 256 tokens: 3 atomics per channel per 256 tokens.  Each double
+// sum and every partial sum the atomics form is exact on the key-mean
+// domain (every partial sum of a channel's keys is a multiple of the
+// channel's smallest key unit below 2^53 of them), so mu does not depend on
+// the order in which units arrive.  (Measured alternatives to the
+// kv_finalize launch: finalizing in the last-arriving workgroup of each
+// group, found by a ticket counter, 9-10 us slower, since every workgroup
+// then waits for its atomics to be performed before it can take a ticket
+// and retire; finalizing in every kv_encode workgroup's prologue, ~5 us
+// slower, since each key workgroup reads all the channels' statistics and
+// divides for every channel.)
+__global__ __launch_bounds__(64 * kStatsWaves) void kv_stats_kernel(
+    const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, int64_t T, int64_t HD,
+    int64_t gy, KvWs w) {
+    __shared__ double sp[kStatsWaves][64][8];  // [wave][lane][channel of the lane]
+    __shared__ float sx[kStatsWaves][64][8];
+    __shared__ float sn[kStatsWaves][64][8];
+    __shared__ float red[kStatsWaves];
     const int h = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int64_t unit = blockIdx.x;
@@ -175,30 +179,45 @@ __global__ __launch_bounds__(128) void kv_stats_kernel(const uint16_t *__restric
     const int64_t chq = y * kGroupCh + lane * 8;
     const bool ch_ok = chq < HD;  // HD is a multiple of 16: all 8 channels or none
     const uint32_t off = ch_ok ? (uint32_t)lane * 8 : 0u;
-    const int64_t t0 = p * kStatsTokens + h * kHalf;
-    const uint16_t *row = (blockIdx.y ? V : K) + y * kGroupCh + t0 * HD;  // wave-uniform
-    const bool full = t0 + kHalf <= T;
-    // descriptor over the wave's rows (32 * HD * 2 bytes < 2^32: HD < 2^26)
     const uint32_t rb = (uint32_t)HD * 2, voff = off * 2;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)row, (short)0, (int)(kHalf * rb), kBufferWord3);
+    const uint16_t *X = blockIdx.y ? V : K;
+    // batch q of this wave: tokens t0 .. t0 + 31 from `row` (wave-uniform),
+    // through a descriptor over its rows (32 * HD * 2 bytes < 2^32: HD < 2^26)
+    auto batch = [&](int q, int64_t &t0, const uint16_t *&row, __amdgpu_buffer_rsrc_t &rs) {
+        t0 = p * kStatsTokens + (h * kStatsBatches + q) * kHalf;
+        row = X + y * kGroupCh + t0 * HD;
+        rs = __builtin_amdgcn_make_buffer_rsrc((void *)row, (short)0, (int)(kHalf * rb),
+                                               kBufferWord3);
+    };
     if (blockIdx.y) {
         float m = 0.0f;
-        if (full) {
-            u32x4 r[kHalf];
-            stats_load(r, rs, voff, 0, rb);
 #pragma unroll
-            for (int j = 0; j < kHalf; ++j) m = stats_value_token(r[j], m);
-        } else {
+        for (int q = 0; q < kStatsBatches; ++q) {
+            int64_t t0;
+            const uint16_t *row;
+            __amdgpu_buffer_rsrc_t rs;
+            batch(q, t0, row, rs);
+            if (t0 + kHalf <= T) {
+                u32x4 r[kHalf];
+                stats_load(r, rs, voff, 0, rb);
+#pragma unroll
+                for (int j = 0; j < kHalf; ++j) m = stats_value_token(r[j], m);
+            } else {
 #pragma unroll 1
-            for (int64_t j = 0; t0 + j < T; ++j)
-                m = stats_value_token(*(const u32x4 *)(row + j * HD + off), m);
+                for (int64_t j = 0; t0 + j < T; ++j)
+                    m = stats_value_token(*(const u32x4 *)(row + j * HD + off), m);
+            }
         }
         m = ch_ok ? m : 0.0f;
         m = wave_max(m);
         if (lane == 0) red[h] = m;
         __syncthreads();
-        if (threadIdx.x == 0) atomicMax(&w.vmax[y], __float_as_uint(fmaxf(red[0], red[1])));
+        if (threadIdx.x == 0) {
+            float a = red[0];
+#pragma unroll
+            for (int v = 1; v < kStatsWaves; ++v) a = fmaxf(a, red[v]);
+            atomicMax(&w.vmax[y], __float_as_uint(a));
+        }
     } else {
         float mx[8], mn[8];
         double a[8], b[8];
@@ -208,33 +227,48 @@ __global__ __launch_bounds__(128) void kv_stats_kernel(const uint16_t *__restric
             mn[i] = __builtin_huge_valf();
             a[i] = b[i] = 0.0;
         }
-        if (full) {
-            u32x4 r[kHalf];
-            stats_load(r, rs, voff, 0, rb);
 #pragma unroll
-            for (int j = 0; j < kHalf / 2; ++j) stats_key_token(r[j], a, mx, mn);
+        for (int q = 0; q < kStatsBatches; ++q) {
+            int64_t t0;
+            const uint16_t *row;
+            __amdgpu_buffer_rsrc_t rs;
+            batch(q, t0, row, rs);
+            if (t0 + kHalf <= T) {
+                u32x4 r[kHalf];
+                stats_load(r, rs, voff, 0, rb);
 #pragma unroll
-            for (int j = kHalf / 2; j < kHalf; ++j) stats_key_token(r[j], b, mx, mn);
-        } else {
+                for (int j = 0; j < kHalf / 2; ++j) stats_key_token(r[j], a, mx, mn);
+#pragma unroll
+                for (int j = kHalf / 2; j < kHalf; ++j) stats_key_token(r[j], b, mx, mn);
+            } else {
 #pragma unroll 1
-            for (int64_t j = 0; t0 + j < T; ++j)
-                stats_key_token(*(const u32x4 *)(row + j * HD + off), a, mx, mn);
+                for (int64_t j = 0; t0 + j < T; ++j)
+                    stats_key_token(*(const u32x4 *)(row + j * HD + off), a, mx, mn);
+            }
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            sp[h][i][lane] = a[i] + b[i];
-            sx[h][i][lane] = mx[i];
-            sn[h][i][lane] = mn[i];
+            sp[h][lane][i] = a[i] + b[i];
+            sx[h][lane][i] = mx[i];
+            sn[h][lane][i] = mn[i];
         }
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < kGroupCh / 128; ++j) {
-            const int c = (int)threadIdx.x + 128 * j, i = c & 7, l = c >> 3;  // lane l, slot i
+        for (int j = 0; j < kGroupCh / (64 * kStatsWaves); ++j) {
+            const int c = (int)threadIdx.x + 64 * kStatsWaves * j, i = c & 7, l = c >> 3;
             const int64_t ch = y * kGroupCh + c;
             if (ch < HD) {
-                unsafeAtomicAdd(&w.sum[ch], sp[0][i][l] + sp[1][i][l]);
-                atomicMax(&w.kmax[ch], ord_bits(fmaxf(sx[0][i][l], sx[1][i][l])));
-                atomicMax(&w.kneg[ch], ord_bits(-fminf(sn[0][i][l], sn[1][i][l])));
+                double s = sp[0][l][i];
+                float x = sx[0][l][i], n = sn[0][l][i];
+#pragma unroll
+                for (int v = 1; v < kStatsWaves; ++v) {
+                    s += sp[v][l][i];
+                    x = fmaxf(x, sx[v][l][i]);
+                    n = fminf(n, sn[v][l][i]);
+                }
+                unsafeAtomicAdd(&w.sum[ch], s);
+                atomicMax(&w.kmax[ch], ord_bits(x));
+                atomicMax(&w.kneg[ch], ord_bits(-n));
             }
         }
     }
@@ -475,7 +509,7 @@ hipError_t kv_noalloc_scratch(void **ptr, size_t *bytes, hipStream_t s) {
 }
 
 hipError_t launch_kv_store(const KvStoreArgs &a, hipStream_t s) {
-    const int64_t nt64 = (a.T + kStatsTokens - 1) / kStatsTokens;
+    const int64_t nodes = (a.T + kStatsTokens - 1) / kStatsTokens;
     const int64_t gy = (a.HD + kGroupCh - 1) / kGroupCh;
     KvWs w = carve_ws(a.ws, a.HD);
     if (a.clear_ws) {
@@ -486,7 +520,8 @@ hipError_t launch_kv_store(const KvStoreArgs &a, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     const unsigned ny = a.v_amax_in ? 1u : 2u;
-    NVFP4_LAUNCH("kv_stats", kv_stats_kernel, dim3((unsigned)(nt64 * gy), ny), dim3(128), 0, s,
+    NVFP4_LAUNCH("kv_stats", kv_stats_kernel, dim3((unsigned)(nodes * gy), ny),
+                 dim3(64 * kStatsWaves), 0, s,
                  a.K, a.V, a.T, a.HD, gy, w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
