@@ -99,7 +99,16 @@ __device__ __forceinline__ void encode_prologue(const float *__restrict__ partia
     if (amax_in) {
         m = *amax_in;
     } else {
-        for (int i = threadIdx.x; i < np; i += blockDim.x) m = fmaxf(m, partials[i]);
+        // four loads per thread in flight before any is used (the partials
+        // come from another kernel: each round trip is a memory latency)
+        const int st = (int)blockDim.x;
+        for (int i = threadIdx.x; i < np; i += 4 * st) {
+            const float a = partials[i];
+            const float b = i + st < np ? partials[i + st] : 0.0f;
+            const float c = i + 2 * st < np ? partials[i + 2 * st] : 0.0f;
+            const float d = i + 3 * st < np ? partials[i + 3 * st] : 0.0f;
+            m = fmaxf(fmaxf(m, a), fmaxf(fmaxf(b, c), d));
+        }
         m = wave_max(m);
     }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
