@@ -157,13 +157,13 @@ __device__ __forceinline__ void load_frag_general(Frag &f, const FragPtr &p, int
 
 // MFMA substep s (K positions 8 s .. 8 s + 7 of each lane half) over the
 // wave's 4 x 3 blocks: block s / 2 of the half, scale byte s / 2.
-template <int S>
-__device__ __forceinline__ void substep(f32x16 (&acc)[FM][FN], const Frag (&A)[FM],
+template <int S, int FMT>
+__device__ __forceinline__ void substep(f32x16 (&acc)[FMT][FN], const Frag (&A)[FMT],
                                         const Frag (&B)[FN]) {
     constexpr int c = S >> 2, i4 = S & 3, hi = (S >> 1) & 1;
-    f16x8 a[FM], b[FN];
+    f16x8 a[FMT], b[FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < FMT; ++i) {
         const f16x2 sg = sigma_pair<c>(A[i].sc);
         const _Float16 g = hi ? sg.y : sg.x;
         a[i] = expand8(dword_of(A[i].q[c], i4), f16x2{g, g});
@@ -175,7 +175,7 @@ __device__ __forceinline__ void substep(f32x16 (&acc)[FM][FN], const Frag (&A)[F
         b[j] = expand8(dword_of(B[j].q[c], i4), f16x2{g, g});
     }
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FMT; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
@@ -195,9 +195,10 @@ struct StageSrc {
     uint32_t a[BM / 32], w[BN / 32], asr, wsr;
 };
 
-template <bool SCALES, bool W2D>
+template <bool SCALES, bool W2D, int FMT = FM>
 __device__ __forceinline__ void stage_src(StageSrc &q, const GemmArgs &g, int64_t m0, int64_t n0,
                                           int wave, int lane) {
+    constexpr int BMT = 64 * FMT;  // tile rows
     const int64_t kbytes = g.K >> 1, KB = g.K >> 4;
     q.ac = __builtin_amdgcn_make_buffer_rsrc((void *)g.a_codes, (short)0, (int)(g.M * kbytes),
                                              kBufferWord3);
@@ -212,11 +213,11 @@ __device__ __forceinline__ void stage_src(StageSrc &q, const GemmArgs &g, int64_
     }
     // block parity gives bit 2 of the swizzle key (8 rows per block; both
     // per-wave block counts are even)
-    static_assert((BM / 32) % 2 == 0 && (BN / 32) % 2 == 0, "block parity");
+    static_assert((BMT / 32) % 2 == 0 && (BN / 32) % 2 == 0, "block parity");
     const int rib = lane >> 3;
 #pragma unroll
-    for (int bb = 0; bb < BM / 32; ++bb) {
-        const int64_t row0 = m0 + (wave * (BM / 32) + bb) * 8 + rib;
+    for (int bb = 0; bb < BMT / 32; ++bb) {
+        const int64_t row0 = m0 + (wave * (BMT / 32) + bb) * 8 + rib;
         const int64_t row = row0 < g.M ? row0 : g.M - 1;
         const int gcol = (lane & 7) ^ ((bb & 1) << 2 | rib >> 1);
         q.a[bb] = (uint32_t)(row * kbytes) + gcol * 16;
@@ -241,14 +242,15 @@ __device__ __forceinline__ void stage_src(StageSrc &q, const GemmArgs &g, int64_
 
 // Issue this wave's direct-to-LDS loads of K step kt into `stage` (codes,
 // and with SCALES the NVFP4 block scales).
-template <bool SCALES, bool W2D>
+template <bool SCALES, bool W2D, int FMT = FM>
 __device__ __forceinline__ void stage_load(const StageSrc &q, uint8_t *stage, int64_t kt, int wave,
                                            int lane) {
+    constexpr int BMT = 64 * FMT;
     const uint32_t kc = (uint32_t)kt * 128, ks = (uint32_t)kt * 16;
 #pragma unroll
-    for (int bb = 0; bb < BM / 32; ++bb)
+    for (int bb = 0; bb < BMT / 32; ++bb)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            q.ac, (lvoid)(stage + kAOff + (wave * (BM / 32) + bb) * 1024), 16, q.a[bb], kc, 0, 0);
+            q.ac, (lvoid)(stage + kAOff + (wave * (BMT / 32) + bb) * 1024), 16, q.a[bb], kc, 0, 0);
 #pragma unroll
     for (int bb = 0; bb < BN / 32; ++bb)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -270,14 +272,15 @@ __device__ __forceinline__ void stage_load(const StageSrc &q, uint8_t *stage, in
 // fragment row R, the 16-byte columns 4h .. 4h + 3 (un-swizzled) and the 8
 // scale bytes of its half.  Fragments start on multiples of 32 tile rows, so
 // the swizzle key of row R is (r >> 1) & 7.
-template <bool SCALES, bool W2D>
-__device__ __forceinline__ void stage_read(Frag (&A)[FM], Frag (&B)[FN], const uint8_t *stage,
+template <bool SCALES, bool W2D, int FMT = FM>
+__device__ __forceinline__ void stage_read(Frag (&A)[FMT], Frag (&B)[FN], const uint8_t *stage,
                                            int wm, int wn, int r, int h) {
+    constexpr int WMT = 32 * FMT;
     const int rib = r & 7, key = (r >> 1) & 7;
     if (SCALES) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-            A[i].sc = *(const u32x2 *)(stage + kASOff + (wm * WM + i * 32 + r) * 16 + h * 8);
+        for (int i = 0; i < FMT; ++i)
+            A[i].sc = *(const u32x2 *)(stage + kASOff + (wm * WMT + i * 32 + r) * 16 + h * 8);
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             const int R = wn * WN + j * 32 + r;
@@ -288,18 +291,18 @@ __device__ __forceinline__ void stage_read(Frag (&A)[FM], Frag (&B)[FN], const u
     for (int c = 0; c < 4; ++c) {
         const int slot = ((h * 4 + c) ^ key) * 16 + rib * 128;
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-            A[i].q[c] = *(const u32x4 *)(stage + kAOff + ((wm * WM + i * 32 + r) >> 3) * 1024 + slot);
+        for (int i = 0; i < FMT; ++i)
+            A[i].q[c] = *(const u32x4 *)(stage + kAOff + ((wm * WMT + i * 32 + r) >> 3) * 1024 + slot);
 #pragma unroll
         for (int j = 0; j < FN; ++j)
             B[j].q[c] = *(const u32x4 *)(stage + kBOff + ((wn * WN + j * 32 + r) >> 3) * 1024 + slot);
     }
 }
 
-template <int... S>
-__device__ __forceinline__ void step_all(f32x16 (&acc)[FM][FN], const Frag (&A)[FM],
+template <int FMT, int... S>
+__device__ __forceinline__ void step_all(f32x16 (&acc)[FMT][FN], const Frag (&A)[FMT],
                                          const Frag (&B)[FN], std::integer_sequence<int, S...>) {
-    (substep<S>(acc, A, B), ...);
+    (substep<S, FMT>(acc, A, B), ...);
 }
 
 // LoRA epilogue operands (LORA = true): XA [M, r] and B [N, r] bf16, the
@@ -320,46 +323,56 @@ constexpr int kQLutOff = kQTileBytes;
 constexpr int kQWaveBytes = kQTileBytes + 128 * 8;     // 25600
 static_assert(4 * kQWaveBytes <= kLdsBytes, "fused-encode LDS");
 
-template <bool OUT_BF16, bool KFAST, bool W2D, bool LORA, bool QUANT>
-__global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float *__restrict__ a_sdec,
-                                                        const float *__restrict__ w_sdec,
-                                                        void *__restrict__ yv,
-                                                        float *__restrict__ amax_out, LoraArgs la,
-                                                        QuantOut qo) {
-    const int64_t M = g.M, N = g.N, K = g.K;
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int64_t tn_count = (N + BN - 1) / BN;
-    const int64_t ntiles = ((M + BM - 1) / BM) * tn_count;
-    // XCD-aware tile order: workgroup b runs on XCD b % 8; XCD x takes the
-    // x-th contiguous range of tiles (tiles past 8 * floor(n / 8) map to
-    // themselves).
-    const int64_t b = blockIdx.x;
-    const int64_t per = ntiles / kXcds;
-    const int64_t t = b < per * kXcds ? (b % kXcds) * per + b / kXcds : b;
-    const int64_t m0 = (t / tn_count) * BM, n0 = (t % tn_count) * BN;
+// Rows [0, m1) are covered by 256-row tiles (the first t1 workgroups), rows
+// [m1, M) by 192-row tiles (the rest of the grid): when the 256-row tiles
+// would leave the chip's last round part-empty (7040 x 3072: 448 tiles, 1.72
+// rounds on 256 CUs), a first round of 256-row tiles and a second of 256
+// 192-row tiles take 1.75 tile times instead of 2.  The host chooses m1.
+struct TileSplit {
+    int64_t t1;  // workgroups of 256-row tiles
+    int64_t m1;  // rows they cover: a multiple of 256, or M
+};
 
+// XCD-aware tile order: workgroup b runs on XCD b % 8; XCD x takes the x-th
+// contiguous range of the `count` tiles (tiles past 8 * floor(count / 8) map
+// to themselves).
+__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t count) {
+    const int64_t per = count / kXcds;
+    return b < per * kXcds ? (b % kXcds) * per + b / kXcds : b;
+}
+
+// One tile at (m0, n0) of FMT * 64 rows x 192 columns: 4 waves (2 x 2) of
+// FMT x 3 MFMA blocks each.
+template <bool OUT_BF16, bool KFAST, bool W2D, bool LORA, bool QUANT, int FMT>
+__device__ __forceinline__ void gemm_tile(const GemmArgs &g, int64_t m0, int64_t n0,
+                                          const float *__restrict__ a_sdec,
+                                          const float *__restrict__ w_sdec, void *__restrict__ yv,
+                                          float *__restrict__ amax_out, const LoraArgs &la,
+                                          const QuantOut &qo, uint8_t *lds) {
+    constexpr int WMT = 32 * FMT;
+    const int64_t M = g.M, N = g.N, K = g.K;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = lane >> 5, r = lane & 31, wm = wave >> 1, wn = wave & 1;
-    const int64_t mw = m0 + wm * WM, nw = n0 + wn * WN;
+    const int64_t mw = m0 + wm * WMT, nw = n0 + wn * WN;
     // a wave whose sub-tile lies wholly past the matrix edge computes nothing
     // (it still takes its share of the loads and every barrier)
     const bool active = mw < M && nw < N;
 
-    f32x16 acc[FM][FN];
+    f32x16 acc[FMT][FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FMT; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
     const int64_t nk = (K + BK - 1) / BK;
-    Frag A[FM], B[FN];
+    Frag A[FMT], B[FN];
     if (KFAST) {
         StageSrc src;
-        stage_src<true, W2D>(src, g, m0, n0, wave, lane);
-        stage_load<true, W2D>(src, lds, 0, wave, lane);
+        stage_src<true, W2D, FMT>(src, g, m0, n0, wave, lane);
+        stage_load<true, W2D, FMT>(src, lds, 0, wave, lane);
         // Each iteration: this wave's loads of step kt have landed; after the
         // barrier so have everyone's, and nobody still reads the stage that
         // the loads of step kt + 1 overwrite.  The last iteration reloads its
@@ -370,8 +383,8 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __syncthreads();
                 const int64_t kn = kt + 1 < nk ? kt + 1 : kt;
-                stage_read<true, W2D>(A, B, lds + (kt & 1) * kStage, wm, wn, r, h);
-                stage_load<true, W2D>(src, lds + ((kt + 1) & 1) * kStage, kn, wave, lane);
+                stage_read<true, W2D, FMT>(A, B, lds + (kt & 1) * kStage, wm, wn, r, h);
+                stage_load<true, W2D, FMT>(src, lds + ((kt + 1) & 1) * kStage, kn, wave, lane);
                 step_all(acc, A, B, std::make_integer_sequence<int, NSUB>{});
             }
         } else {
@@ -379,7 +392,7 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __syncthreads();
                 const int64_t kn = kt + 1 < nk ? kt + 1 : kt;
-                stage_load<true, W2D>(src, lds + ((kt + 1) & 1) * kStage, kn, wave, lane);
+                stage_load<true, W2D, FMT>(src, lds + ((kt + 1) & 1) * kStage, kn, wave, lane);
             }
         }
         // no load into LDS is still in flight when the wave leaves
@@ -388,25 +401,20 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
         // is past its last read
         if (QUANT || OUT_BF16) __syncthreads();
     } else if (active) {
-        FragPtr pa[FM], pb[FN];
+        FragPtr pa[FMT], pb[FN];
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < FMT; ++i)
             pa[i] = frag_ptr(g.a_codes, g.a_scales, mw + i * 32 + r, M, K, false, h);
 #pragma unroll
         for (int j = 0; j < FN; ++j)
             pb[j] = frag_ptr(g.w_codes, g.w_scales, nw + j * 32 + r, N, K, W2D, h);
         for (int64_t kt = 0; kt < nk; ++kt) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i) load_frag_general(A[i], pa[i], kt, K, h);
+            for (int i = 0; i < FMT; ++i) load_frag_general(A[i], pa[i], kt, K, h);
 #pragma unroll
             for (int j = 0; j < FN; ++j) load_frag_general(B[j], pb[j], kt, K, h);
             step_all(acc, A, B, std::make_integer_sequence<int, NSUB>{});
         }
-    }
-    if (QUANT && blockIdx.x == 0 && threadIdx.x == 0) {
-        float s_enc, s_dec;
-        tensor_scales(*qo.amax_in, s_enc, s_dec);
-        *qo.s_dec = s_dec;
     }
     if (!active) return;
 
@@ -417,9 +425,9 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
     // of r per step, for two row blocks x three column blocks at a time; each
     // step loads those 2 + 3 fragments at once (rows past the edge are
     // clamped, never stored)
-    constexpr int FH = FM / 2;
+    constexpr int FH = FMT % 2 == 0 ? FMT / 2 : 1;  // row blocks per LoRA pass
 #pragma unroll
-    for (int ih = 0; ih < 2; ++ih) {
+    for (int ih = 0; ih < FMT / FH; ++ih) {
         f32x16 lo[FH][FN];
         if (LORA) {
             const uint16_t *xp[FH], *bp[FN];
@@ -490,7 +498,7 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         constexpr int kPieces = WN / 8;  // 12 a row
 #pragma unroll 4
-        for (int k = 0; k < WM * kPieces / 64; ++k) {
+        for (int k = 0; k < WMT * kPieces / 64; ++k) {
             const int c = lane + 64 * k, rl = c / kPieces, cc = c - rl * kPieces;
             const int64_t row = mw + rl, col = nw + cc * 8;
             const u32x4 v = *(const u32x4 *)(qw + c * 16);
@@ -511,7 +519,7 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         constexpr int kBlkRow = WN / 16;  // 6 blocks a row
 #pragma unroll 2
-        for (int k = 0; k < WM * kBlkRow / 64; ++k) {
+        for (int k = 0; k < WMT * kBlkRow / 64; ++k) {
             const int blk = lane + 64 * k;
             const int rl = blk / kBlkRow, cb = blk - rl * kBlkRow;
             const int64_t row = mw + rl, col = nw + cb * 16;
@@ -537,6 +545,34 @@ __global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, const float 
     }
 }
 
+
+template <bool OUT_BF16, bool KFAST, bool W2D, bool LORA, bool QUANT>
+__global__ __launch_bounds__(256) void gemm_w4a4_kernel(GemmArgs g, TileSplit ts,
+                                                        const float *__restrict__ a_sdec,
+                                                        const float *__restrict__ w_sdec,
+                                                        void *__restrict__ yv,
+                                                        float *__restrict__ amax_out, LoraArgs la,
+                                                        QuantOut qo) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    if (QUANT && blockIdx.x == 0 && threadIdx.x == 0) {
+        float s_enc, s_dec;
+        tensor_scales(*qo.amax_in, s_enc, s_dec);
+        *qo.s_dec = s_dec;
+    }
+    const int64_t tn = (g.N + BN - 1) / BN;
+    const int64_t b = blockIdx.x;
+    if (b < ts.t1) {
+        const int64_t t = xcd_tile(b, ts.t1);
+        gemm_tile<OUT_BF16, KFAST, W2D, LORA, QUANT, FM>(g, (t / tn) * BM, (t % tn) * BN, a_sdec,
+                                                         w_sdec, yv, amax_out, la, qo, lds);
+    } else {
+        const int64_t t = xcd_tile(b - ts.t1, (int64_t)gridDim.x - ts.t1);
+        gemm_tile<OUT_BF16, KFAST, W2D, LORA, QUANT, 3>(g, ts.m1 + (t / tn) * (64 * 3),
+                                                        (t % tn) * BN, a_sdec, w_sdec, yv,
+                                                        amax_out, la, qo, lds);
+    }
+}
+
 // Raise the dynamic-LDS limit of `fns` to `bytes` once per device: `done`
 // holds one bit per device id (0..31) already set up.  Threads that race
 // both set the attribute, which is harmless.
@@ -553,6 +589,71 @@ hipError_t lds_limit_once(const void *const *fns, int n, int bytes,
     }
     done.fetch_or(bit, std::memory_order_release);
     return hipSuccess;
+}
+
+// Compute units of the current device (0 if unknown), cached per device.
+static int device_cus() {
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int c = cache[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            c <= 0)
+            c = -1;
+        cache[dev].store(c, std::memory_order_relaxed);
+    }
+    return c > 0 ? c : 0;
+}
+
+// Finish time, in quarters of a 256-row tile, of n1 256-row tiles then n2
+// 192-row tiles (3 quarters each) handed to `cus` CUs in workgroup order,
+// each to the CU that frees first.  After the first kind every CU is busy
+// until a = 4 floor(n1 / cus), or a + 4 for the n1 mod cus that took one
+// more; a tile of the second kind then starts at the n-th smallest of the
+// times {a + 3 k} and {a + 4 + 3 k} (one sequence per CU), so the last one
+// starts at the smallest T by which n2 starts are available.
+static int64_t split_makespan(int64_t n1, int64_t n2, int cus) {
+    const int64_t q = n1 / cus, r = n1 % cus, a = 4 * q, b = a + 4;
+    const int64_t first = r > 0 ? b : a;
+    if (n2 == 0) return n1 > 0 ? first : 0;
+    auto starts = [&](int64_t t) {  // tile starts of the second kind at or before t
+        int64_t n = 0;
+        if (t >= a) n += (cus - r) * ((t - a) / 3 + 1);
+        if (r > 0 && t >= b) n += r * ((t - b) / 3 + 1);
+        return n;
+    };
+    int64_t lo = a, hi = a + 3 * n2;
+    while (lo < hi) {
+        const int64_t mid = lo + (hi - lo) / 2;
+        if (starts(mid) >= n2)
+            hi = mid;
+        else
+            lo = mid + 1;
+    }
+    return first > lo + 3 ? first : lo + 3;
+}
+
+// The TileSplit of an M x N output: all 256-row tiles, unless moving the
+// last rows to 192-row tiles finishes more than 3% sooner.
+static TileSplit choose_split(int64_t M, int64_t N, int64_t &grid) {
+    const int64_t tn = (N + BN - 1) / BN, kfull = (M + BM - 1) / BM;
+    TileSplit ts{kfull * tn, M};
+    grid = ts.t1;
+    const int cus = device_cus();
+    if (cus <= 0) return ts;
+    const int64_t base = split_makespan(kfull * tn, 0, cus);
+    int64_t best = base;
+    for (int64_t k1 = kfull - 1; k1 >= 0; --k1) {
+        const int64_t k2 = (M - k1 * BM + 191) / 192;
+        const int64_t t = split_makespan(k1 * tn, k2 * tn, cus);
+        if (t < best && t * 100 < base * 97) {
+            best = t;
+            ts = TileSplit{k1 * tn, k1 * BM};
+            grid = (k1 + k2) * tn;
+        }
+    }
+    return ts;
 }
 
 // s_dec of an empty fused-encode output.
@@ -576,7 +677,8 @@ hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, con
                      quant->amax_in, quant->s_dec);
         return hipGetLastError();
     }
-    const int64_t ntiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    int64_t ntiles = 0;
+    const TileSplit ts = choose_split(M, N, ntiles);
     const dim3 grid((unsigned)ntiles);
     const GemmArgs g{a_codes, a_scales, w_codes, w_scales, M, N, K};
     const LoraArgs la{lora_xa, lora_b, lora_r, lora_scale};
@@ -603,8 +705,8 @@ hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, con
 #define NVFP4_GEMM(BF, KF, W2, LO, Q)                                                       \
     NVFP4_LAUNCH(Q ? "gemm_w4a4_quant" : LO ? "gemm_w4a4_lora" : "gemm_w4a4",                \
                  (gemm_w4a4_kernel<BF, KF, W2, LO, Q>), grid, dim3(256),                      \
-                 KF ? kLdsBytes : Q ? 4 * kQWaveBytes : 0, s, g, a_sdec, w_sdec, y, amax_out, \
-                 la, qo)
+                 KF ? kLdsBytes : Q ? 4 * kQWaveBytes : 0, s, g, ts, a_sdec, w_sdec, y,        \
+                 amax_out, la, qo)
 #define NVFP4_GEMM_K(BF, W2, LO, Q)      \
     if (fast)                            \
         NVFP4_GEMM(BF, true, W2, LO, Q); \
