@@ -107,9 +107,23 @@ def test_gemm_attention_projection_sampled(nv, orc):
     shape), 48 sampled rows (first and last M tile included)."""
     print("case: gemm 7040x3072x3072 sampled", flush=True)
     qa, qw = operands(orc, 7040, 3072, 3072, 1003, w_std=0.02)
-    rows = np.unique(np.concatenate([[0, 1, 127, 6912, 7039],
+    # on 256 CUs rows 0..4095 go in 256-row tiles and 4096..7039 in 192-row
+    # tiles: both sides of that boundary and of the 192-row tiles' edges
+    rows = np.unique(np.concatenate([[0, 1, 127, 4095, 4096, 4287, 4288, 6912, 6911, 7039],
                                      np.random.default_rng(1).integers(0, 7040, 43)]))
     check(nv, orc, qa, qw, torch.bfloat16, rows=rows)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_gemm_split_tiles_ragged_tail(nv, orc, out_dtype):
+    """4296 x 3072 x 512: on 256 CUs 272 tiles of 256 rows would take two
+    rounds, so rows 4096..4295 go in two 192-row tiles (the second holds 8
+    rows); every output row near the boundaries and a random sample."""
+    print("case: gemm 4296x3072x512 split tiles", out_dtype, flush=True)
+    qa, qw = operands(orc, 4296, 3072, 512, 1005, w_std=0.02)
+    rows = np.unique(np.concatenate([np.arange(4088, 4296),
+                                     np.random.default_rng(2).integers(0, 4088, 40)]))
+    check(nv, orc, qa, qw, out_dtype, rows=rows)
 
 
 @pytest.mark.parametrize("N,K", [(14336, 3072), (3072, 14336)], ids=["ffn_up", "ffn_down"])
