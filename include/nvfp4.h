@@ -385,6 +385,20 @@ int nvfp4_gather_window(const nvfp4_kv_ring *ring, int64_t step, void *K_out, vo
                         int64_t capacity_tokens, int64_t *n_tokens, void *stream);
 
 /*
+ * Launch shape nvfp4_gemm_w4a4 (and its variants) takes for an M x N output
+ * on a device with `compute_units` CUs (pure host; the launch asks the
+ * device for its count).  The output's first *rows_256 rows go in 256 x 192
+ * tiles and the rest in 192 x 192 tiles, *workgroups in all: 192-row tiles
+ * for the last rows only where greedy in-order dispatch of the two kinds of
+ * tile onto the CUs finishes more than 3% sooner than all 256-row tiles (a
+ * 192-row tile taken as 3/4 of a 256-row one).  Results do not depend on the
+ * split.  M, N >= 0, compute_units >= 1, non-NULL outputs, else
+ * NVFP4_EINVAL.
+ */
+int nvfp4_gemm_plan(int64_t M, int64_t N, int32_t compute_units, int64_t *rows_256,
+                    int64_t *workgroups);
+
+/*
  * Attention of step `step`'s queries over K_eff(step), read packed from the
  * ring with the dequantization fused in (DeepRead summary, Multi-Shot
  * Attention Sink: sliding-window self-attention over K_eff(t) = A_g u A_s u

@@ -86,6 +86,8 @@ _EXPORTS = {
                            C.c_void_p, C.c_void_p], C.c_int),
     "nvfp4_gemm_mx": ([C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_int64,
                        C.c_int64, C.c_void_p, C.c_int32, C.c_void_p], C.c_int),
+    "nvfp4_gemm_plan": ([C.c_int64, C.c_int64, C.c_int32, C.POINTER(C.c_int64),
+                         C.POINTER(C.c_int64)], C.c_int),
     "nvfp4_kv_ring_bytes": ([C.POINTER(CKvConfig)], C.c_size_t),
     "nvfp4_kv_store_workspace_bytes": ([C.POINTER(CKvConfig)], C.c_size_t),
     "nvfp4_kv_ring_init": ([C.POINTER(CKvRing), C.POINTER(CKvConfig), C.c_void_p, C.c_size_t],
@@ -295,6 +297,14 @@ def gemm_w4a4_quant(a: NVFP4Tensor, w: NVFP4Tensor, amax_in: torch.Tensor,
     _check(lib().nvfp4_gemm_w4a4_quant(C.byref(ca), C.byref(cw), C.byref(cy), search, pin, pout,
                                        _stream(stream)))
     return out
+
+
+def gemm_plan(M: int, N: int, compute_units: int):
+    """nvfp4_gemm_plan: (rows in 256-row tiles, workgroups) of the W4A4 grid
+    for an M x N output on `compute_units` CUs (pure host)."""
+    r, g = C.c_int64(), C.c_int64()
+    _check(lib().nvfp4_gemm_plan(M, N, compute_units, C.byref(r), C.byref(g)))
+    return r.value, g.value
 
 
 def lora_down(x: torch.Tensor, a: torch.Tensor, out: torch.Tensor | None = None,

@@ -639,6 +639,15 @@ static int attn_setup(const nvfp4_kv_ring *ring, int64_t step, int64_t n_q, int3
     return hip_status(e, "attention: device query");
 }
 
+int nvfp4_gemm_plan(int64_t M, int64_t N, int32_t compute_units, int64_t *rows_256,
+                    int64_t *workgroups) {
+    if (!rows_256 || !workgroups) return fail(NVFP4_EINVAL, "gemm_plan: NULL output");
+    if (M < 0 || N < 0 || compute_units < 1)
+        return fail(NVFP4_EINVAL, "gemm_plan: M, N must be >= 0 and compute_units >= 1");
+    nvfp4::gemm_plan(M, N, compute_units, rows_256, workgroups);
+    return ok();
+}
+
 int nvfp4_attention_plan(const nvfp4_kv_ring *ring, int64_t step, int64_t n_q, int32_t key_splits,
                          int32_t *splits, size_t *ws_bytes) {
     if (!splits || !ws_bytes) return fail(NVFP4_EINVAL, "attention_plan: NULL output");

@@ -634,14 +634,15 @@ static int64_t split_makespan(int64_t n1, int64_t n2, int cus) {
     return first > lo + 3 ? first : lo + 3;
 }
 
-// The TileSplit of an M x N output: all 256-row tiles, unless moving the
-// last rows to 192-row tiles finishes more than 3% sooner.
-static TileSplit choose_split(int64_t M, int64_t N, int64_t &grid) {
+// The row split of an M x N output on `cus` compute units: rows [0, *m1) in
+// 256-row tiles, the rest in 192-row tiles, *grid workgroups.  All 256-row
+// tiles unless moving the last rows to 192-row tiles finishes more than 3%
+// sooner (the earliest finish wins; among equals, the most 256-row tiles).
+void gemm_plan(int64_t M, int64_t N, int cus, int64_t *m1, int64_t *grid) {
     const int64_t tn = (N + BN - 1) / BN, kfull = (M + BM - 1) / BM;
-    TileSplit ts{kfull * tn, M};
-    grid = ts.t1;
-    const int cus = device_cus();
-    if (cus <= 0) return ts;
+    *m1 = M;
+    *grid = kfull * tn;
+    if (cus <= 0 || M <= 0 || N <= 0) return;
     const int64_t base = split_makespan(kfull * tn, 0, cus);
     int64_t best = base;
     for (int64_t k1 = kfull - 1; k1 >= 0; --k1) {
@@ -649,11 +650,18 @@ static TileSplit choose_split(int64_t M, int64_t N, int64_t &grid) {
         const int64_t t = split_makespan(k1 * tn, k2 * tn, cus);
         if (t < best && t * 100 < base * 97) {
             best = t;
-            ts = TileSplit{k1 * tn, k1 * BM};
-            grid = (k1 + k2) * tn;
+            *m1 = k1 * BM;
+            *grid = (k1 + k2) * tn;
         }
     }
-    return ts;
+}
+
+// The TileSplit of an M x N output on the current device.
+static TileSplit choose_split(int64_t M, int64_t N, int64_t &grid) {
+    int64_t m1 = M;
+    gemm_plan(M, N, device_cus(), &m1, &grid);
+    const int64_t tn = (N + BN - 1) / BN;
+    return TileSplit{((m1 + BM - 1) / BM) * tn, m1};
 }
 
 // s_dec of an empty fused-encode output.

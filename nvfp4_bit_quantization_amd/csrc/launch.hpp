@@ -160,6 +160,9 @@ hipError_t launch_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales, con
                             void *y, int ydtype, float *amax_out, const uint16_t *lora_xa,
                             const uint16_t *lora_b, int64_t lora_r, float lora_scale,
                             const QuantOut *quant, hipStream_t s);
+// Row split of the W4A4 grid for `cus` compute units (rows [0, *m1) in
+// 256-row tiles, the rest in 192-row tiles) and its workgroup count.
+void gemm_plan(int64_t M, int64_t N, int cus, int64_t *m1, int64_t *grid);
 hipError_t launch_lora_down(const uint16_t *x, const uint16_t *a, int64_t M, int64_t K, int64_t r,
                             uint16_t *xa, hipStream_t s);
 hipError_t launch_gemm_mx(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *w_codes,

@@ -87,6 +87,18 @@ int main() {
     EXPECT(launched_or_ok(nvfp4_mx_quantize(F, 1, 64, 256, FB, FB, nullptr)));
     EXPECT(nvfp4_mx_quantize(F, 1, 64, 48, FB, FB, nullptr) == NVFP4_ESHAPE);
     EXPECT(launched_or_ok(nvfp4_gemm_mx(FB, FB, FB, FB, 64, 32, 512, F, 1, nullptr)));
+    for (int64_t m = 0; m < 9000; m += 137)
+        for (int32_t cus : {1, 7, 256}) {
+            int64_t r = -1, wg = -1;
+            EXPECT(nvfp4_gemm_plan(m, 3072, cus, &r, &wg) == NVFP4_OK);
+            EXPECT((r == m || r % 256 == 0) && r <= m && wg >= 0);
+            EXPECT(wg == ((r + 255) / 256 + (m - r + 191) / 192) * 16);
+        }
+    {
+        int64_t r, wg;
+        EXPECT(nvfp4_gemm_plan(-1, 1, 1, &r, &wg) == NVFP4_EINVAL);
+        EXPECT(nvfp4_gemm_plan(1, 1, 0, &r, &wg) == NVFP4_EINVAL);
+    }
     EXPECT(nvfp4_gemm_mx(FB, FB, FB, FB, 64, 32, 500, F, 1, nullptr) == NVFP4_ESHAPE);
 
     // KV ring: many small configurations, the plan checked against brute force
