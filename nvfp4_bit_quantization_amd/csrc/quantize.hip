@@ -343,8 +343,11 @@ hipError_t launch_amax(const void *x, int dtype, int64_t n, float *partials, int
 int amax_partials_for(int64_t n) { return grid_for(n / 8, 256 * 4, kMaxPartials); }
 
 // Workgroups of the streaming kernels: enough to fill every CU several
-// times, few enough that the per-workgroup prologue stays small.
+// times, few enough that the per-workgroup prologue stays small.  The plain
+// 1-D encode runs best with two a CU (7040 x 3072 bf16: 14.3-14.5 us at 512
+// workgroups, 14.9-15.2 at 1024, 15.4-16.1 at 768, 15.7-16.3 at 2048).
 constexpr int kStreamGrid = 1024;
+constexpr int kEncode1dGrid = 512;
 
 hipError_t launch_encode(const void *x, int dtype, int64_t rows, int64_t cols, int layout,
                          int search, const float *partials, int np, const float *amax_in,
@@ -354,7 +357,7 @@ hipError_t launch_encode(const void *x, int dtype, int64_t rows, int64_t cols, i
     uint32_t *c32 = (uint32_t *)codes;
     if (layout == 0) {
         const int64_t nblk = n / 16;
-        const int g = grid_for(nblk, 256, kStreamGrid);
+        const int g = grid_for(nblk, 256, kEncode1dGrid);
         uint2 *c64 = (uint2 *)codes;
         const bool buf = n * (dtype == kF32 ? 4 : 2) < ((int64_t)1 << 31);
 #define L1(T, F)                                                                            \
