@@ -300,6 +300,14 @@ __device__ __forceinline__ void store8(uint16_t *p, const float (&y)[8]) {
                         pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
 }
 
+// The same as a non-temporal (streaming) store: the line is not kept dirty
+// in the caches for a later write-back.
+__device__ __forceinline__ void store8_stream(uint16_t *p, const float (&y)[8]) {
+    const u32x4 v = u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
+                          pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
+    __builtin_nontemporal_store(v, (u32x4 *)p);
+}
+
 // x_hat_i = RN(V(q_i) * S) for the 8 codes of dword q.
 __device__ __forceinline__ void dequant8(uint32_t q, float S, float (&y)[8]) {
     f32x2 v;
