@@ -29,9 +29,10 @@
 //
 // Tiling: workgroup 4 waves (2 x 2), tile BM x BN = 256 x 192; each wave owns
 // 128 x 96 = 4 x 3 blocks of v_mfma_f32_32x32x16_f16 (192 fp32 accumulators
-// per lane).  Workgroups are mapped to tiles XCD by XCD: XCD x takes the x-th
-// contiguous (row-major) range of tiles, so tiles that share operand rows
-// share an L2.
+// per lane).  Where it shortens the last round, the last rows go in 192 x 192
+// tiles (96 x 96 = 3 x 3 blocks a wave) in the same launch (TileSplit).
+// Workgroups are mapped to tiles XCD by XCD: XCD x takes the x-th contiguous
+// (row-major) range of tiles, so tiles that share operand rows share an L2.
 //
 // Data flow (K % 256 == 0): the packed tiles of a K step (codes 128 bytes
 // per row, scales 16 bytes per row or 16-row group) go from memory straight
