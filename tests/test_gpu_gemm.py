@@ -114,6 +114,20 @@ def test_gemm_attention_projection_sampled(nv, orc):
     check(nv, orc, qa, qw, torch.bfloat16, rows=rows)
 
 
+@pytest.mark.parametrize("K", [512, 272])
+def test_gemm_256_row_tiles_only(nv, orc, K):
+    """4096 x 3072: on 256 CUs exactly one round of 256-row tiles, so no row
+    goes to a 192-row tile; K = 272 takes the general (per-lane load) path."""
+    print("case: gemm 4096x3072 all 256-row tiles, K", K, flush=True)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if cus == 256:
+        assert nv.gemm_plan(4096, 3072, cus) == (4096, 256)
+    qa, qw = operands(orc, 4096, 3072, K, 1006, w_std=0.02)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 4095],
+                                     np.random.default_rng(3).integers(0, 4096, 40)]))
+    check(nv, orc, qa, qw, torch.float32, rows=rows)
+
+
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_gemm_split_tiles_ragged_tail(nv, orc, out_dtype):
     """4296 x 3072 x 512: on 256 CUs 272 tiles of 256 rows would take two
