@@ -27,7 +27,8 @@
 //                V, writing the ring slot and, for sink chunks, the sink copy
 //                in the same pass
 // Gather = one launch: workgroups take runs of tokens of one segment (ring
-// slot or sink copy) of the effective set, a lane per half block.
+// slot or sink copy) of the effective set, a lane per half block, the bf16
+// output written with non-temporal stores.
 #include <mutex>
 
 #include "device.hpp"
