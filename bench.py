@@ -789,7 +789,7 @@ def main():
     kt = kernel_times(nv, step, args.steps, args.warmup + args.steps)
     dom = max(kt, key=lambda k: kt[k][0] * kt[k][1])
     per_launch = {"kv_encode": kv_bytes_per_chunk(), "kv_gather": kv_bytes_per_chunk(),
-                  "kv_stats": 2 * KV_T * KV_H * KV_D * 2, "kv_finalize": KV_H * KV_D * 4 + 8}
+                  "kv_stats": 2 * KV_T * KV_H * KV_D * 2}
     k_ms = kt[dom][1]
     achieved = per_launch[dom] / k_ms / 1e6
     cache = {"kv_stats": "cold: reads the step's chunk from HBM (4 rotated input sets) while "

@@ -343,7 +343,8 @@ int nvfp4_kv_begin_shot(nvfp4_kv_ring *ring, int64_t chunk_idx);
  *   of chunk 0 clears them first (one small extra launch).  So one workspace
  *   serves one ring's stores, or several rings' stores one after another;
  *   two stores sharing a workspace must not overlap.
- * Three launches (four for chunk 0): statistics, finalize, encode.
+ * Two launches (three for chunk 0): statistics (whose last workgroup of
+ *   each channel group finalizes the group's mean and amax), encode.
  */
 int nvfp4_kv_store_chunk(nvfp4_kv_ring *ring, int64_t chunk_idx, const void *K_bf16,
                          const void *V_bf16, const float *v_amax_in, void *workspace,

@@ -11,17 +11,17 @@
 // removed.  The Italian page ("Inferenza W4A4 NVFP4") adds that the KV cache
 // uses micro-block scaling with the Four Over Six selection.
 //
-// Store = three launches:
+// Store = two launches:
 //   kv_stats     four waves per (256-token node, 512 channels): per-channel key
 //                sums in double, key max / min and the value |max| over the
 //                node, added into the workspace with device-scope atomics
 //                (the sums are exact on the key-mean domain, so their order
-//                does not matter)
-//   kv_finalize  one workgroup per 512-channel group: mu = (float)(S / T),
-//                the group's key amax max_c max(RN(max K - mu), RN(mu - min K))
-//                (equal to the elementwise amax of RN(K - mu) because RN is
-//                monotone) and value amax, and the accumulators cleared for
-//                the next call
+//                does not matter); the last workgroup of each 512-channel
+//                group to finish then finalizes the group: mu = (float)(S /
+//                T), the group's key amax max_c max(RN(max K - mu), RN(mu -
+//                min K)) (equal to the elementwise amax of RN(K - mu) because
+//                RN is monotone) and value amax, and the accumulators cleared
+//                for the next call
 //   kv_encode    the FP32 tensor scales of K_s and V from the groups'
 //                amaxes, then the 1-D 4/6 encoder over K_s = RN(K - mu) and
 //                V, writing the ring slot and, for sink chunks, the sink copy
@@ -44,14 +44,15 @@ constexpr int kGroupCh = 512;         // channels per stats unit (64 lanes x 8)
 constexpr int64_t kEncodeGrid = 4096; // encode workgroups per tensor (upper bound)
 constexpr int64_t kEncodeBlocks = 6;  // target blocks per encode lane (measured: 6 over ~10)
 
-// Store workspace.  The accumulators are zero between calls: every store
-// leaves them so (kv_finalize clears them), and a store of chunk 0 clears
-// them first.
+// Store workspace.  The accumulators and ticket counters are zero between
+// calls: every store leaves them so (the finalizing workgroups clear them),
+// and a store of chunk 0 clears them first.
 struct KvWs {
     double *sum;     // [HD] per-channel key sums
     uint32_t *kmax;  // [HD] order-preserving bits of the channel's key max
     uint32_t *kneg;  // [HD] order-preserving bits of minus the channel's key min
     uint32_t *vmax;  // [gy] value |max| of each channel group (float bits)
+    uint32_t *tick;  // [gy] statistics workgroups of each group done
     float *gamax;    // [gy] this call's key amax of each channel group (read by kv_encode)
     float *gvmax;    // [gy] this call's value amax of each channel group
 };
@@ -70,6 +71,8 @@ static KvWs carve_ws(void *ws, int64_t HD) {
     p += align256(HD * 4);
     w.vmax = (uint32_t *)p;
     p += align256(gy * 4);
+    w.tick = (uint32_t *)p;
+    p += align256(gy * 4);
     w.gamax = (float *)p;
     p += align256(gy * 4);
     w.gvmax = (float *)p;
@@ -79,7 +82,7 @@ static KvWs carve_ws(void *ws, int64_t HD) {
 // The part that must be zero between calls, and the whole.
 static int64_t kv_ws_zero_bytes(int64_t HD) {
     const int64_t gy = (HD + kGroupCh - 1) / kGroupCh;
-    return align256(HD * 8) + 2 * align256(HD * 4) + align256(gy * 4);
+    return align256(HD * 8) + 2 * align256(HD * 4) + 2 * align256(gy * 4);
 }
 size_t kv_store_ws_bytes(int64_t T, int64_t HD) {
     (void)T;
@@ -159,17 +162,31 @@ __device__ __forceinline__ float stats_value_token(const u32x4 &r, float m) {
 // sum and every partial sum the atomics form is exact on the key-mean
 // domain (every partial sum of a channel's keys is a multiple of the
 // channel's smallest key unit below 2^53 of them), so mu does not depend on
-// the order in which units arrive.  (Measured alternatives to the
-// kv_finalize launch: finalizing in the last-arriving workgroup of each
-// group, found by a ticket counter, 9-10 us slower, since every workgroup
-// then waits for its atomics to be performed before it can take a ticket
-// and retire; finalizing in every kv_encode workgroup's prologue, ~5 us
-// slower, since each key workgroup reads all the channels' statistics and
-// divides for every channel.)
+// the order in which units arrive.
+//
+// Finalize: each wave waits until its atomics are performed (s_waitcnt
+// vmcnt(0)), the workgroup meets at a barrier, and thread 0 takes a ticket
+// of its channel group (a relaxed device-scope atomic add); the workgroup
+// that takes the group's last ticket (per_group: the group's key and value
+// units) finalizes the group.  Every other unit's atomics were performed
+// before its ticket was taken, and the finalizing workgroup reads the
+// accumulators with device-scope atomic loads, so it sees them all.  With
+// one round of workgroups (every unit resident at once) the wait before the
+// ticket delays nothing else: the store is ~2 us faster than with a
+// separate finalize launch (7040 x 24 x 128, 66.7 -> 64.6 us a KV step);
+// with 64-token units (1320 workgroups queued behind waiting ones) the same
+// scheme was 9-10 us slower.  (Finalizing in every kv_encode workgroup's
+// prologue instead: ~5 us slower, since each key workgroup reads all the
+// channels' statistics and divides for every channel.)
+__device__ __forceinline__ void finalize_group(const KvWs &w, int64_t y, int64_t T, int64_t HD,
+                                               float *mu_slot, float *mu_g, float *mu_s,
+                                               float *red);
+
 __global__ __launch_bounds__(64 * kStatsWaves) void kv_stats_kernel(
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, int64_t T, int64_t HD,
-    int64_t gy, KvWs w) {
-    __shared__ double sp[kStatsWaves][64][8];  // [wave][lane][channel of the lane]
+    int64_t gy, KvWs w, float *mu_slot, float *mu_g, float *mu_s, uint32_t per_group) {
+    __shared__ double sp[kStatsWaves][64][8];
+    __shared__ int last;  // [wave][lane][channel of the lane]
     __shared__ float sx[kStatsWaves][64][8];
     __shared__ float sn[kStatsWaves][64][8];
     __shared__ float red[kStatsWaves];
@@ -273,21 +290,27 @@ __global__ __launch_bounds__(64 * kStatsWaves) void kv_stats_kernel(
             }
         }
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's atomics performed
+    __syncthreads();
+    if (threadIdx.x == 0)
+        last = __hip_atomic_fetch_add(&w.tick[y], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               per_group - 1;
+    __syncthreads();
+    if (last) finalize_group(w, y, T, HD, mu_slot, mu_g, mu_s, red);
 }
 
-// One workgroup per 512-channel group y, two channels a thread (loads issued
-// first): mu = (float)(S / T) into the slot (and the sink copies), the
-// group's key amax max_c max(RN(max K - mu), RN(mu - min K)) and value amax
-// for kv_encode; the group's sums, extrema and value maximum go back to zero
-// for the next call.  The accumulators are read and cleared with
-// device-scope atomic loads and stores (coherent across the chip's L2
-// caches, like the atomics that filled them).
-__global__ __launch_bounds__(256) void kv_finalize_kernel(KvWs w, int64_t T, int64_t HD,
-                                                          float *mu_slot, float *mu_g,
-                                                          float *mu_s) {
-    __shared__ float red[4];
+// Finalize channel group y (one workgroup of 256 threads, two channels a
+// thread, loads issued first): mu = (float)(S / T) into the slot (and the
+// sink copies), the group's key amax max_c max(RN(max K - mu), RN(mu - min
+// K)) and value amax for kv_encode; the group's sums, extrema, value maximum
+// and ticket counter go back to zero for the next call.  The accumulators
+// are read and cleared with device-scope atomic loads and stores (coherent
+// across the chip's L2 caches, like the atomics that filled them).  `red`:
+// 4 floats of LDS.
+__device__ __forceinline__ void finalize_group(const KvWs &w, int64_t y, int64_t T, int64_t HD,
+                                               float *mu_slot, float *mu_g, float *mu_s,
+                                               float *red) {
     constexpr int kPer = kGroupCh / 256;
-    const int64_t y = blockIdx.x;
     double S[kPer];
     uint32_t xo[kPer], no[kPer];
 #pragma unroll
@@ -322,8 +345,10 @@ __global__ __launch_bounds__(256) void kv_finalize_kernel(KvWs w, int64_t T, int
         w.gamax[y] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
         w.gvmax[y] = __uint_as_float(vb);
         __hip_atomic_store(&w.vmax[y], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&w.tick[y], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
+
 
 // Zero the store workspace (the first store of a ring).
 __global__ __launch_bounds__(256) void kv_ws_clear_kernel(uint32_t *__restrict__ p, int64_t n4) {
@@ -476,7 +501,7 @@ __global__ __launch_bounds__(256) void kv_encode_kernel(
 constexpr int64_t kNoallocMaxHD = 16384;
 constexpr size_t kNoallocScratchBytes =
     (size_t)(((kNoallocMaxHD * 8 + 255) & ~255) + 2 * ((kNoallocMaxHD * 4 + 255) & ~255) +
-             3 * 256);
+             4 * 256);
 static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
 
 int64_t kv_noalloc_max_hd() { return kNoallocMaxHD; }
@@ -523,13 +548,10 @@ hipError_t launch_kv_store(const KvStoreArgs &a, hipStream_t s) {
     const unsigned ny = a.v_amax_in ? 1u : 2u;
     NVFP4_LAUNCH("kv_stats", kv_stats_kernel, dim3((unsigned)(nodes * gy), ny),
                  dim3(64 * kStatsWaves), 0, s,
-                 a.K, a.V, a.T, a.HD, gy, w);
+                 a.K, a.V, a.T, a.HD, gy, w, a.slot.mu,
+                 a.g_tokens > 0 ? a.gsink.mu : (float *)nullptr,
+                 a.s_tokens > 0 ? a.ssink.mu : (float *)nullptr, (uint32_t)(nodes * ny));
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    NVFP4_LAUNCH("kv_finalize", kv_finalize_kernel, dim3((unsigned)gy), dim3(256), 0, s, w, a.T,
-                 a.HD, a.slot.mu, a.g_tokens > 0 ? a.gsink.mu : (float *)nullptr,
-                 a.s_tokens > 0 ? a.ssink.mu : (float *)nullptr);
-    e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nblk = a.T * a.HD / 16;
     // Grid: about kEncodeBlocks blocks per lane (whole iterations of the

@@ -177,8 +177,9 @@ def test_ring_validation(L):
     assert L.nvfp4_kv_store_chunk(C.byref(r), 0, FAKE, FAKE, None, FAKE, ws - 1, None) == -4
     assert L.nvfp4_kv_store_chunk(C.byref(r), 0, FAKE + 2, FAKE, None, FAKE, ws, None) == -2
     assert L.nvfp4_kv_store_chunk(C.byref(r), 0, FAKE, FAKE, FAKE + 2, FAKE, ws, None) == -2
-    # sums, max, min per channel; value max, key and value amax per 512-channel group
-    assert ws == 3072 * 16 + 3 * 256
+    # sums, max, min per channel; value max, ticket counter, key and value amax
+    # per 512-channel group
+    assert ws == 3072 * 16 + 4 * 256
     assert L.nvfp4_kv_begin_shot(C.byref(r), 3) == -5
     n = C.c_int64()
     assert L.nvfp4_kv_effective_tokens(C.byref(r), 1, C.byref(n)) == -5
