@@ -276,25 +276,26 @@ def test_gather_capacity_error(nv):
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("search", [1, 0], ids=["4o6", "6only"])
 @pytest.mark.parametrize("factor", [1.0, 2.5, 0.5])
-def test_store_value_amax_from_producer(nv, orc, factor):
+def test_store_value_amax_from_producer(nv, orc, factor, search):
     """The value tensor scale from a producer's amax (the statistics pass then
     reads the keys only): with the true max|V| the ring holds the same bytes
     as a plain store; with another amax the value codes, scales and decode
     scale are the oracle's quantization of V with that amax (values beyond
-    it saturate), the keys unchanged."""
+    it saturate), the keys unchanged.  Both scale searches."""
     Lf, Fc, H, d = 40, 5, 3, 128
     T, HD = Lf * Fc, H * d
-    print("case: store with producer value amax x", factor, flush=True)
+    print("case: store with producer value amax x", factor, "search", search, flush=True)
     cfg = nv.KVConfig(tokens_per_frame=Lf, frames_per_chunk=Fc, heads=H, head_dim=d,
-                      sink_frames_global=1, sink_frames_shot=1, window_chunks=2)
+                      sink_frames_global=1, sink_frames_shot=1, window_chunks=2, search=search)
     Kg, Vg, K, V = chunk_inputs(2400, 0, T, H, d)
     vmax = np.float32(np.abs(V).max() * np.float32(factor))
     ring = nv.KVRing(cfg)
     ring.store_chunk(0, Kg, Vg, v_amax=torch.tensor([vmax], dtype=torch.float32, device="cuda"))
     mem = ring_bytes(ring)
-    ref = orc.kv_encode_chunk(K, V)
-    vc, vs, sdv = orc.quantize(V, amax=float(vmax))
+    ref = orc.kv_encode_chunk(K, V, search=search)
+    vc, vs, sdv = orc.quantize(V, amax=float(vmax), search=search)
     ref.update(vc=vc, vs=vs, sdv=sdv)
     assert_region(region(mem, 0, T, HD), ref, T, HD)
     assert_region(region(mem, ring.ring.gsink_offset, Lf, HD), ref, Lf, HD)
@@ -305,3 +306,26 @@ def test_store_value_amax_from_producer(nv, orc, factor):
         for off, n in ((0, T), (ring.ring.gsink_offset, Lf), (ring.ring.ssink_offset, Lf)):
             got, want = region(mem, off, n, HD), region(pm, off, n, HD)
             assert all(np.array_equal(got[k], want[k]) for k in got)
+
+
+def test_store_value_amax_full_chunk_matches_plain(nv):
+    """The 5B model's whole chunk (7040 tokens x 24 heads x 128, three sink
+    frames each): a store given the true max|V| writes the same slot and
+    sink bytes as a plain store (whose bytes the oracle checks above)."""
+    Lf, Fc, H, d = 880, 8, 24, 128
+    T, HD = Lf * Fc, H * d
+    print("case: full chunk, producer value amax vs plain store", flush=True)
+    cfg = nv.KVConfig(tokens_per_frame=Lf, frames_per_chunk=Fc, heads=H, head_dim=d,
+                      sink_frames_global=3, sink_frames_shot=3, window_chunks=2)
+    kb, vb = synth.kv_chunk(2600, 0, T, H, d, threads=THREADS)
+    Kg = torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16).cuda()
+    Vg = torch.from_numpy(vb.view(np.int16)).view(torch.bfloat16).cuda()
+    vmax = Vg.float().abs().max().reshape(1).contiguous()
+    a, b = nv.KVRing(cfg), nv.KVRing(cfg)
+    a.store_chunk(0, Kg, Vg, v_amax=vmax)
+    b.store_chunk(0, Kg, Vg)
+    ma, mb = ring_bytes(a), ring_bytes(b)
+    for off, n in ((0, T), (a.ring.gsink_offset, 3 * Lf), (a.ring.ssink_offset, 3 * Lf)):
+        got, want = region(ma, off, n, HD), region(mb, off, n, HD)
+        for k in got:
+            assert np.array_equal(got[k], want[k]), (off, k)
