@@ -85,10 +85,31 @@ __global__ __launch_bounds__(256) void amax_rht_kernel(const T *__restrict__ x, 
     if (threadIdx.x == 0) partials[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-// Reduce `np` partial maxima (or take *amax_in), derive the tensor scales and
-// build the per-scale-code table (S, r): S = RN(sigma * s_dec), r = RN(1 / S)
-// (0 when S == 0).  Called by every workgroup of the encode kernels.
-__device__ __forceinline__ void encode_prologue(const float *__restrict__ partials, int np,
+// This thread's first four amax partials (i, i + blockDim, ...; zero past
+// `np`), loaded together; nothing is loaded when the amax is given.  Issued
+// before a kernel's first data loads: the loads return in order, so partials
+// requested after the data would wait for the data too.
+struct Partials4 {
+    float a, b, c, d;
+};
+__device__ __forceinline__ Partials4 partials_issue(const float *__restrict__ partials, int np,
+                                                    const float *__restrict__ amax_in) {
+    Partials4 p{0.0f, 0.0f, 0.0f, 0.0f};
+    if (amax_in) return p;
+    const int st = (int)blockDim.x, i = (int)threadIdx.x;
+    if (i < np) p.a = partials[i];
+    if (i + st < np) p.b = partials[i + st];
+    if (i + 2 * st < np) p.c = partials[i + 2 * st];
+    if (i + 3 * st < np) p.d = partials[i + 3 * st];
+    return p;
+}
+
+// Reduce `np` partial maxima (the first four per thread already loaded in
+// `p`; or take *amax_in), derive the tensor scales and build the
+// per-scale-code table (S, r): S = RN(sigma * s_dec), r = RN(1 / S) (0 when
+// S == 0).  Called by every workgroup of the encode kernels.
+__device__ __forceinline__ void encode_prologue(const Partials4 &p,
+                                                const float *__restrict__ partials, int np,
                                                 const float *__restrict__ amax_in,
                                                 float *__restrict__ s_dec_out, f32x2 *lut,
                                                 float &s_enc_out) {
@@ -99,16 +120,9 @@ __device__ __forceinline__ void encode_prologue(const float *__restrict__ partia
     if (amax_in) {
         m = *amax_in;
     } else {
-        // four loads per thread in flight before any is used (the partials
-        // come from another kernel: each round trip is a memory latency)
+        m = fmaxf(fmaxf(p.a, p.b), fmaxf(p.c, p.d));
         const int st = (int)blockDim.x;
-        for (int i = threadIdx.x; i < np; i += 4 * st) {
-            const float a = partials[i];
-            const float b = i + st < np ? partials[i + st] : 0.0f;
-            const float c = i + 2 * st < np ? partials[i + 2 * st] : 0.0f;
-            const float d = i + 3 * st < np ? partials[i + 3 * st] : 0.0f;
-            m = fmaxf(fmaxf(m, a), fmaxf(fmaxf(b, c), d));
-        }
+        for (int i = threadIdx.x + 4 * st; i < np; i += st) m = fmaxf(m, partials[i]);
         m = wave_max(m);
     }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -153,11 +167,12 @@ __device__ __forceinline__ void candidate(const float (&x)[8], float am, float s
 
 // With RHT every block is first transformed by rht16 (signs).  BUF (arrays
 // below 2^31 bytes): raw buffer loads and stores with 32-bit offsets, the
-// first two blocks of each lane requested before the prologue and two kept
-// in flight, the loop unrolled three times so the block registers rotate
-// without copies; a block past the end loads as zero and its stores are
-// dropped by the range check.  Otherwise: two blocks per iteration by
-// pointer.
+// amax partials and then the first two blocks of each lane requested before
+// the prologue and two blocks kept in flight, the loop unrolled three times
+// so the block registers rotate without copies; a block past the end loads as
+// zero and is not encoded (the last iteration's empty slots would otherwise
+// cost a sixth of the encode work at 7040 x 3072 on 512 workgroups).
+// Otherwise: two blocks per iteration by pointer.
 template <typename T, bool FOUR_OVER_SIX, bool RHT, bool BUF>
 __global__ __launch_bounds__(256) void encode1d_kernel(
     const T *__restrict__ x, int64_t nblk, const float *__restrict__ partials, int np,
@@ -172,11 +187,12 @@ __global__ __launch_bounds__(256) void encode1d_kernel(
             (void *)x, (short)0, (int)(nb * BB), kBufferWord3);
         auto off = [nb](uint32_t blk) { return (blk < nb ? blk : nb) * BB; };
         uint32_t b = blockIdx.x * blockDim.x + threadIdx.x;
+        const Partials4 pp = partials_issue(partials, np, amax_in);
         Raw ra, rb, rc;
         buffer_load16(xr, off(b), ra);
         buffer_load16(xr, off(b + stride), rb);
         float s_enc;
-        encode_prologue(partials, np, amax_in, s_dec_out, lut, s_enc);
+        encode_prologue(pp, partials, np, amax_in, s_dec_out, lut, s_enc);
         const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
             (void *)codes, (short)0, (int)(nb * 8u), kBufferWord3);
         const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
@@ -194,14 +210,15 @@ __global__ __launch_bounds__(256) void encode1d_kernel(
             buffer_load16(xr, off(b + 2 * stride), rc);
             encode(ra, b);
             buffer_load16(xr, off(b + 3 * stride), ra);
-            encode(rb, b + stride);
+            if (b + stride < nb) encode(rb, b + stride);
             buffer_load16(xr, off(b + 4 * stride), rb);
-            encode(rc, b + 2 * stride);
+            if (b + 2 * stride < nb) encode(rc, b + 2 * stride);
         }
         return;
     }
     float s_enc;
-    encode_prologue(partials, np, amax_in, s_dec_out, lut, s_enc);
+    encode_prologue(partials_issue(partials, np, amax_in), partials, np, amax_in, s_dec_out,
+                    lut, s_enc);
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += 2 * stride) {
         const int64_t b2 = b + stride;
@@ -238,7 +255,8 @@ __global__ __launch_bounds__(256) void encode2d_kernel(
     uint8_t *__restrict__ scales, float *__restrict__ s_dec_out) {
     __shared__ f32x2 lut[128];
     float s_enc;
-    encode_prologue(partials, np, amax_in, s_dec_out, lut, s_enc);
+    encode_prologue(partials_issue(partials, np, amax_in), partials, np, amax_in, s_dec_out,
+                    lut, s_enc);
     const int64_t tcols = cols >> 4, trows = rows >> 4;
     const int64_t ntiles = trows * tcols;
     const int lane32 = threadIdx.x & 31;
