@@ -75,31 +75,49 @@ def bf16_from_bits(bits, device):
     return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(device)
 
 
-def time_steps(step_fn, steps, warmup, per_step=False):
+WARMUP_MIN_S = 0.25  # every timing warms up for at least this long (clocks settle)
+
+
+def time_steps(step_fn, steps, warmup, per_step=False, warm_s=WARMUP_MIN_S):
     """Mean ms per step over `steps` steps bracketed by synchronisations (and
-    the wall-clock mean).  With per_step, also the median of the steps' own
-    durations, from an event recorded after every step on the current
-    stream."""
+    the wall-clock mean), after `warmup` untimed steps and at least `warm_s`
+    seconds of untimed steps (the shader clock takes about a tenth of a
+    second of sustained work to settle: back-to-back W4A4 GEMMs went 136 ->
+    124 -> 118 us a call over the first runs).  Nothing but the steps runs
+    between the two synchronisations.  With per_step, a second pass of
+    `steps` steps records an event after every step and gives the median of
+    the steps' own durations (each such event adds ~2.5 us to a step on this
+    GPU, so the mean is taken from the first pass)."""
     import torch
 
-    for i in range(warmup):
+    i = 0
+    t0 = time.perf_counter()
+    while i < warmup or time.perf_counter() - t0 < warm_s:
         step_fn(i)
+        i += 1
+        if i >= warmup and i % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1 if per_step else 2)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     w0 = time.perf_counter()
     ev[0].record(s)
-    for i in range(steps):
-        step_fn(warmup + i)
-        if per_step:
-            ev[i + 1].record(s)
-    ev[-1].record(s)
+    for k in range(steps):
+        step_fn(i + k)
+    ev[1].record(s)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - w0) * 1e3
-    mean = ev[0].elapsed_time(ev[-1]) / steps
+    mean = ev[0].elapsed_time(ev[1]) / steps
     if not per_step:
         return mean, wall / steps
-    med = statistics.median(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    i += steps
+    pe = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    pe[0].record(s)
+    for k in range(steps):
+        step_fn(i + k)
+        pe[k + 1].record(s)
+    torch.cuda.synchronize()
+    med = statistics.median(pe[k].elapsed_time(pe[k + 1]) for k in range(steps))
     return mean, wall / steps, med
 
 
