@@ -823,7 +823,8 @@ def main():
             "cache": cache.get(dom, "")}
 
     out = {"metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "steps": args.steps, "warmup": args.warmup, "warmup_min_s": WARMUP_MIN_S,
+           "ms_per_step": round(ms, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
            "data": "synthetic",
            "config": {"workload": "kv_chunk_quant_dequant", "tokens": KV_T, "heads": KV_H,
